@@ -1,0 +1,153 @@
+"""Plant plausible mistakes in the oracle and require that a pin catches each.
+
+Every mutant below is a deliberately wrong variant of one oracle function (a
+dropped term, a wrong sign or index, a transposed operand, a wrong scale).  It
+is patched into ``oracle.llama_ref`` for the duration of one test, and the pins
+of oracle_pins.py are run until one fails.  A mutant that passes every pin
+would mean the pins cannot tell that mistake from the truth.
+"""
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import llama_ref as R
+
+F64 = np.float64
+
+
+def _rmsnorm_eps_outside(x, gamma, eps):
+    x = np.asarray(x, F64)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * gamma
+
+
+def _rmsnorm_no_gamma(x, gamma, eps):
+    x = np.asarray(x, F64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _rmsnorm_across_tokens(x, gamma, eps):
+    x = np.asarray(x, F64)
+    return x / np.sqrt(np.mean(x * x) + eps) * gamma
+
+
+def _rope_generic(sign=1.0, half=False, freq_div=1.0):
+    def rope(z, positions, rope_theta):
+        z = np.asarray(z, F64)
+        hd = z.shape[-1]
+        i = np.arange(hd // 2, dtype=F64)
+        inv = np.power(F64(rope_theta), -2.0 * i / hd / freq_div)
+        ang = sign * np.asarray(positions, F64)[:, None] * inv[None, :]
+        c = np.cos(ang)[:, None, :]
+        s = np.sin(ang)[:, None, :]
+        out = np.empty_like(z)
+        if half:
+            a, b = z[..., :hd // 2], z[..., hd // 2:]
+            out[..., :hd // 2] = a * c - b * s
+            out[..., hd // 2:] = a * s + b * c
+        else:
+            a, b = z[..., 0::2], z[..., 1::2]
+            out[..., 0::2] = a * c - b * s
+            out[..., 1::2] = a * s + b * c
+        return out
+    return rope
+
+
+def _attention_generic(scale="sqrt", strict=False, mod_map=False, normalise=True):
+    def attn(q, k, v, q_pos):
+        q, k, v = (np.asarray(a, F64) for a in (q, k, v))
+        T, nh, hd = q.shape
+        S, nkv, _ = k.shape
+        g = nh // nkv
+        kp = np.arange(S)
+        vis = (kp[None, :] < np.asarray(q_pos)[:, None]) if strict else (kp[None, :] <= np.asarray(q_pos)[:, None])
+        o = np.empty((T, nh, hd))
+        for h in range(nh):
+            j = (h % nkv) if mod_map else (h // g)
+            s = q[:, h, :] @ k[:, j, :].T
+            s = s / {"sqrt": np.sqrt(F64(hd)), "none": 1.0, "lin": F64(hd)}[scale]
+            s = np.where(vis, s, -np.inf)
+            e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+            p = e / np.sum(e, axis=-1, keepdims=True) if normalise else e
+            o[:, h, :] = p @ v[:, j, :]
+        return o
+    return attn
+
+
+def _sigmoid_not_silu(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, F64)))
+
+
+def _greedy_last_tie(logits):
+    a = np.asarray(logits)
+    return a.shape[-1] - 1 - np.argmax(a[..., ::-1], axis=-1)
+
+
+def _layer_generic(drop_attn_residual=False, rotate_v=False, wo_transposed=False,
+                   cache_pre_rope=False, swap_gate_up=False, drop_ffn_residual=False):
+    def layer(cfg, w, x, k_cache, v_cache, start_pos, out_rows=None):
+        x = np.asarray(x, F64)
+        T = x.shape[0]
+        nh, nkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+        pos = start_pos + np.arange(T)
+        u = R.rmsnorm(x, w.attn_norm, cfg.eps)
+        q = (u @ w.w_q.T).reshape(T, nh, hd)
+        k = (u @ w.w_k.T).reshape(T, nkv, hd)
+        v = (u @ w.w_v.T).reshape(T, nkv, hd)
+        q = R.rope(q, pos, cfg.rope_theta)
+        kr = R.rope(k, pos, cfg.rope_theta)
+        if rotate_v:
+            v = R.rope(v, pos, cfg.rope_theta)
+        k_cache[:, pos, :] = (k if cache_pre_rope else kr).transpose(1, 0, 2)
+        v_cache[:, pos, :] = v.transpose(1, 0, 2)
+        rows = np.arange(T) if out_rows is None else np.asarray(out_rows)
+        S = start_pos + T
+        o = R.causal_gqa_attention(q[rows], k_cache[:, :S].transpose(1, 0, 2),
+                                   v_cache[:, :S].transpose(1, 0, 2), pos[rows])
+        wo = w.w_o.T if wo_transposed else w.w_o
+        attn = o.reshape(len(rows), nh * hd) @ wo.T
+        h1 = attn if drop_attn_residual else x[rows] + attn
+        u2 = R.rmsnorm(h1, w.ffn_norm, cfg.eps)
+        if swap_gate_up:
+            f = (R.silu(u2 @ w.w_up.T) * (u2 @ w.w_gate.T)) @ w.w_down.T
+        else:
+            f = R.swiglu_ffn(u2, w)
+        return f if drop_ffn_residual else h1 + f
+    return layer
+
+
+MUTANTS = {
+    "rmsnorm_eps_outside_sqrt": ("rmsnorm", _rmsnorm_eps_outside),
+    "rmsnorm_drops_gamma": ("rmsnorm", _rmsnorm_no_gamma),
+    "rmsnorm_across_tokens": ("rmsnorm", _rmsnorm_across_tokens),
+    "rope_wrong_sign": ("rope", _rope_generic(sign=-1.0)),
+    "rope_half_split_pairs": ("rope", _rope_generic(half=True)),
+    "rope_wrong_frequencies": ("rope", _rope_generic(freq_div=2.0)),
+    "attention_no_scale": ("causal_gqa_attention", _attention_generic(scale="none")),
+    "attention_scale_1_over_d": ("causal_gqa_attention", _attention_generic(scale="lin")),
+    "attention_mask_excludes_self": ("causal_gqa_attention", _attention_generic(strict=True)),
+    "gqa_head_modulo_mapping": ("causal_gqa_attention", _attention_generic(mod_map=True)),
+    "softmax_unnormalised": ("causal_gqa_attention", _attention_generic(normalise=False)),
+    "silu_is_sigmoid": ("silu", _sigmoid_not_silu),
+    "greedy_last_index_on_tie": ("greedy", _greedy_last_tie),
+    "layer_drops_attention_residual": ("_layer_one_sequence", _layer_generic(drop_attn_residual=True)),
+    "layer_drops_ffn_residual": ("_layer_one_sequence", _layer_generic(drop_ffn_residual=True)),
+    "layer_rotates_v": ("_layer_one_sequence", _layer_generic(rotate_v=True)),
+    "layer_wo_transposed": ("_layer_one_sequence", _layer_generic(wo_transposed=True)),
+    "layer_caches_k_before_rope": ("_layer_one_sequence", _layer_generic(cache_pre_rope=True)),
+    "layer_swaps_gate_and_up": ("_layer_one_sequence", _layer_generic(swap_gate_up=True)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(R, attr, fn)
+    caught = []
+    for check in P.ALL_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except (AssertionError, ValueError, IndexError) as e:
+            caught.append((check.__name__, type(e).__name__))
+            break
+    assert caught, f"mutant {name} passed every pin"
