@@ -1,0 +1,251 @@
+"""Benchmark of the decoder layer on one MI355X.
+
+A step is one call of the layer (every step of the hot path) on one batch of
+seeded synthetic input already resident in HBM.  The default workload is the
+7B-shaped layer decoding one token against a 4096-position cache; the JSON line
+also carries the layer's algorithmic HBM rate, the roofline of its dominant
+kernel (timed with HIP events around that kernel's launches on its stream, over
+the timed steps) and the fp64 oracle timed on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s per layer (HBM GB/s %) and prefill TFLOP/s (MFMA %), 1 GPU"
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def layer_weight_elems(s) -> int:
+    H, nh, nkv, hd, I = s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate
+    return (nh + 2 * nkv) * hd * H + H * nh * hd + 2 * I * H + H * I
+
+
+def decode_bytes(s, ctx_len, act_b, kv_b) -> dict:
+    """Algorithmic HBM bytes of one decode call: each weight once, each cached
+    K/V entry that is attended once, the new K/V entries, x, y and the gains."""
+    B = len(ctx_len)
+    kv_read = int(np.sum(np.asarray(ctx_len, np.int64) + 1)) * s.n_kv_heads * s.head_dim * 2 * kv_b
+    w = layer_weight_elems(s) * act_b
+    small = B * s.hidden * act_b * 2 + 2 * s.hidden * act_b + B * 2 * s.n_kv_heads * s.head_dim * kv_b
+    gate_up = 2 * s.intermediate * s.hidden * act_b + B * (s.hidden + s.intermediate) * act_b
+    return {"total": w + kv_read + small, "weights": w, "kv_read": kv_read, "gemv_gate_up": gate_up}
+
+
+def prefill_flops(s, T) -> dict:
+    H, nh, nkv, hd, I = s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate
+    f = {"qkv": 2 * T * H * (nh + 2 * nkv) * hd, "o": 2 * T * nh * hd * H,
+         "gate_up": 2 * T * H * 2 * I, "down": 2 * T * I * H,
+         "attention": 4 * hd * nh * T * (T + 1) // 2}
+    f["total"] = sum(f.values())
+    return f
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline_decode(wl, stored, inp, budget_s: float) -> dict:
+    """The fp64 oracle (as it stands) on the same decode workload, repeated
+    until `budget_s` seconds of CPU work have run."""
+    from llama2_decoder_layer_amd import synth as S
+    from oracle import llama_ref as R
+    s = wl.shape
+    cfg = R.LayerConfig(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.eps,
+                        s.rope_theta)
+    w = R.LayerWeights(**{k: S.to_f64(v, wl.act_dtype) for k, v in stored.items()})
+    B = wl.batch
+    nb = B if B <= 4 else 4  # bounded sample: the first sequences of the batch
+    kc = S.to_f64(inp["k_cache"][:nb], wl.kv_dtype)
+    vc = S.to_f64(inp["v_cache"][:nb], wl.kv_dtype)
+    x = S.to_f64(inp["x"][:nb], wl.act_dtype)
+    ctx = inp["ctx_len"][:nb]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        R.layer_decode(cfg, w, x, kc, vc, ctx)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": n * nb / el, "unit": "tokens/s/layer", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{n} oracle decode calls of {nb} sequence(s) of this workload in {el:.1f} s"}
+
+
+def cpu_baseline_prefill(wl, stored, inp, budget_s: float) -> dict:
+    from llama2_decoder_layer_amd import synth as S
+    from oracle import llama_ref as R
+    s = wl.shape
+    cfg = R.LayerConfig(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.eps,
+                        s.rope_theta)
+    w = R.LayerWeights(**{k: S.to_f64(v, wl.act_dtype) for k, v in stored.items()})
+    T = 64
+    while True:  # grow the prompt until one prefill takes a measurable share of the budget
+        x = S.to_f64(inp["x"][:1, :T], wl.act_dtype)
+        kc = np.zeros((1, s.n_kv_heads, T, s.head_dim))
+        vc = np.zeros_like(kc)
+        t0 = time.perf_counter()
+        R.layer_prefill(cfg, w, x, kc, vc, 0)
+        el = time.perf_counter() - t0
+        if el > budget_s / 4 or T >= wl.tokens:
+            break
+        T = min(wl.tokens, T * 2)
+    fl = prefill_flops(s, T)["total"]
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"one oracle prefill of the first {T} tokens of this workload in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_7b_b1_ctx4096",
+                    choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096"])
+    ap.add_argument("--copies", type=int, default=0,
+                    help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from llama2_decoder_layer_amd import binding as B
+    from llama2_decoder_layer_amd import synth as S
+
+    wl = S.WORKLOADS[args.workload]
+    s = wl.shape
+    act, kvd = wl.act_dtype, wl.kv_dtype
+    act_b, kv_b = S.DTYPE_BYTES[act], S.DTYPE_BYTES[kvd]
+    print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
+    stored, inp = S.workload_layer_and_inputs(wl.name)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+    def dev(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "f32":
+            return torch.from_numpy(a).cuda()
+        return torch.from_numpy(a.view(np.int16)).cuda().view(tdt[dt])
+
+    per_copy = layer_weight_elems(s) * act_b + 2 * inp["k_cache"].size * kv_b
+    copies = args.copies or max(1, min(8, -(-1_500_000_000 // per_copy)))
+    max_pos = wl.s_max
+    cfg = B.make_config(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.eps,
+                        s.rope_theta, act, kvd, max_pos)
+    rc = torch.empty(max_pos, s.head_dim // 2, dtype=torch.float32, device="cuda")
+    rs = torch.empty_like(rc)
+    B.llama_rope_table(rc, rs, max_pos, s.head_dim, s.rope_theta)
+    sets = []
+    for c in range(copies):
+        w = {k: dev(v, act) for k, v in stored.items()}
+        w["rope_cos"], w["rope_sin"] = rc, rs
+        sets.append((B.LayerWeights(w), dev(inp["k_cache"], kvd), dev(inp["v_cache"], kvd)))
+    decode = wl.phase == "decode"
+    if decode:
+        x = dev(inp["x"], act)
+        y = torch.empty_like(x)
+        ctx = torch.from_numpy(inp["ctx_len"]).cuda()
+        max_ctx = int(inp["ctx_len"].max())
+        ws = torch.empty(B.llama_layer_workspace_size(cfg, wl.batch, 1, wl.s_max), dtype=torch.uint8,
+                         device="cuda")
+
+        def step(i):
+            lw, kc, vc = sets[i % copies]
+            B.llama_layer_decode(cfg, lw, x, y, kc, vc, ctx, wl.batch, max_ctx, wl.s_max, ws)
+        dom = "gemv_gate_up"
+    else:
+        x = dev(inp["x"], act)
+        y = torch.empty_like(x)
+        ws = torch.empty(B.llama_layer_workspace_size(cfg, wl.batch, wl.tokens, wl.s_max),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            lw, kc, vc = sets[i % copies]
+            B.llama_layer_prefill(cfg, lw, x, y, kc, vc, wl.batch, wl.tokens, 0, wl.s_max, ws)
+        dom = "gemm_gate_up"
+
+    print(f"[bench] {copies} copies, warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kid = B.kernel_id(dom)
+    B.llama_layer_timer_start(kid, args.steps)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kms, kn = B.llama_layer_timer_stop()
+    ms_step = el * 1e3 / args.steps
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": act, "data": "synthetic (seeded; see synth.py)"}
+    kavg_s = kms / 1e3 / max(kn, 1)
+    if decode:
+        by = decode_bytes(s, inp["ctx_len"], act_b, kv_b)
+        out.update(value=wl.batch / (ms_step / 1e3), unit="tokens/s/layer")
+        layer_gbps = by["total"] / (ms_step / 1e3) / 1e9
+        out["layer_hbm"] = {"bytes_per_step": by["total"], "GBps": layer_gbps,
+                            "frac_of_peak": layer_gbps / HBM_PEAK_GBPS}
+        ach = by[dom] / kavg_s / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                           "algorithmic_bytes_per_launch": by[dom], "avg_launch_us": kavg_s * 1e6,
+                           "launches_timed": kn}
+    else:
+        fl = prefill_flops(s, wl.tokens)
+        tflops = fl["total"] / (ms_step / 1e3) / 1e12
+        out.update(value=tflops, unit="TFLOP/s")
+        out["layer_mfma"] = {"flops_per_step": fl["total"], "TFLOPs": tflops,
+                             "frac_of_peak": tflops / BF16_PEAK_TFLOPS}
+        ach = fl["gate_up"] / kavg_s / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                           "algorithmic_flops_per_launch": fl["gate_up"],
+                           "avg_launch_us": kavg_s * 1e6, "launches_timed": kn}
+    out["config"] = {"workload": wl.name, "hidden": s.hidden, "n_heads": s.n_heads,
+                     "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
+                     "intermediate": s.intermediate, "batch": wl.batch,
+                     "tokens": wl.tokens if not decode else 1,
+                     "ctx": (wl.ctx if wl.ctx else list(wl.ctx_range)) if decode else 0,
+                     "kv_dtype": kvd, "rotating_copies": copies}
+    if decode and wl.ctx_range:
+        out["config"]["ctx_len_sum"] = int(np.sum(inp["ctx_len"]))
+    if args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    else:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        if decode:
+            out["cpu_baseline"] = cpu_baseline_decode(wl, stored, inp, args.cpu_budget)
+        else:
+            out["cpu_baseline"] = cpu_baseline_prefill(wl, stored, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * llama_layer.h -- C ABI of the MI355X (gfx950) Llama-2 decoder layer.
+ *
+ * One call runs one pre-norm decoder layer for a batch of sequences:
+ *
+ *   u   = RMSNorm(x; attn_norm, eps)                 per token, eps inside the root
+ *   q,k,v = u W_q^T, u W_k^T, u W_v^T                split into heads of head_dim
+ *   q,k = RoPE(q,k; position)                        adjacent pairs (2i, 2i+1) turned
+ *                                                    by position * rope_theta^(-2i/head_dim)
+ *   K/V cache[b, j, position, :] = k, v              append (k after RoPE)
+ *   o_h = softmax(q_h K_j^T / sqrt(head_dim) + causal mask) V_j,  j = h / (n_heads/n_kv_heads)
+ *   h1  = x + o W_o^T
+ *   out = h1 + (silu(u2 W_gate^T) * (u2 W_up^T)) W_down^T,   u2 = RMSNorm(h1; ffn_norm, eps)
+ *
+ * Definitions: "Llama2架构与推理全解析：从原理到KV Cache与量化部署" §1.2 (RMSNorm),
+ * §1.3 (SwiGLU), §1.4 (RoPE), §1.5 (GQA), §2.1 (prefill / decode), §2.3 (the
+ * per-layer recipe and residual stream), §2.4 (KV cache); "Llama2架构全景解析"
+ * §1.1 (pre-norm, RoPE as multiplication by e^{i m theta}), §1.2 (query heads
+ * sharing one K/V head); "LLM架构全景解析：从基础模块到工程实践" §2.2 (the cache
+ * object written at the current position).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers unless stated otherwise, dense,
+ *    row-major, 16-byte aligned (int32 id/length arrays and float32 logits:
+ *    4-byte aligned).  The caller owns every buffer; the library
+ *    never allocates or frees device memory and never synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t of the calling process's HIP
+ *    runtime; NULL = the null stream) and runs asynchronously.
+ *  - Weights are stored [out_features, in_features] (y = x W^T).
+ *  - Return 0 on success, a negative LL_E* code otherwise.  Arguments are
+ *    validated on the host before anything is enqueued, so a call that fails
+ *    validation has no side effect.  Faults inside kernels surface at the
+ *    caller's next synchronisation, as with any asynchronous API.
+ *  - Calls are stateless; distinct buffers may be used from several host
+ *    threads at once.  Calls that share a workspace must be ordered (same
+ *    stream, or synchronised).
+ */
+#ifndef LLAMA_LAYER_H
+#define LLAMA_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats. */
+typedef enum { LL_F32 = 0, LL_BF16 = 1, LL_F16 = 2 } ll_dtype;
+
+/* Error codes. */
+enum {
+  LL_OK = 0,
+  LL_EINVAL = -1,       /* bad configuration or size                         */
+  LL_ENULL = -2,        /* a required pointer is NULL                        */
+  LL_EALIGN = -3,       /* a pointer is not 16-byte aligned                  */
+  LL_ECACHE_FULL = -4,  /* positions would run past the cache capacity s_max */
+  LL_EWORKSPACE = -5,   /* workspace missing or smaller than required        */
+  LL_EHIP = -6,         /* the HIP runtime reported an error at launch       */
+  LL_EUNSUPPORTED = -7  /* valid but not implemented (e.g. head_dim 96)      */
+};
+
+/*
+ * Layer hyper-parameters, named as in the size table of
+ * "Llama2架构与推理全解析" §1.6.
+ *   hidden        model width H (multiple of 8)
+ *   n_heads       query heads
+ *   n_kv_heads    key/value heads; n_heads % n_kv_heads == 0 (GQA; == MHA when equal)
+ *   head_dim      64 or 128; n_heads * head_dim must be a multiple of 8
+ *   intermediate  SwiGLU width I (multiple of 8)
+ *   eps           RMSNorm epsilon (> 0)
+ *   rope_theta    RoPE base (> 1)
+ *   act_dtype     format of weights, gains, x and y: LL_F32 or LL_BF16 (or LL_F16)
+ *   kv_dtype      format of the K/V caches: LL_F32, LL_BF16 or LL_F16
+ *                 (LL_F32 caches require act_dtype LL_F32)
+ *   max_pos       rows of rope_cos / rope_sin; every position used must be < max_pos
+ */
+typedef struct {
+  int32_t hidden, n_heads, n_kv_heads, head_dim, intermediate;
+  float eps, rope_theta;
+  int32_t act_dtype, kv_dtype;
+  int32_t max_pos;
+} ll_config;
+
+/*
+ * One layer's parameters (device pointers, act_dtype unless noted).
+ *   attn_norm [H]                  gain of the attention RMSNorm
+ *   w_q [n_heads*head_dim, H]      w_k, w_v [n_kv_heads*head_dim, H]
+ *   w_o [H, n_heads*head_dim]
+ *   ffn_norm [H]                   gain of the FFN RMSNorm
+ *   w_gate, w_up [I, H]            w_down [H, I]
+ *   rope_cos, rope_sin  float32 [max_pos, head_dim/2]: cos/sin(m * theta_i),
+ *                       as written by llama_rope_table().
+ */
+typedef struct {
+  const void *attn_norm, *w_q, *w_k, *w_v, *w_o, *ffn_norm, *w_gate, *w_up, *w_down;
+  const float *rope_cos, *rope_sin;
+} ll_weights;
+
+/*
+ * Bytes of device workspace a prefill (tokens = T) or decode (tokens = 1)
+ * call with this configuration needs; 0 if the configuration is invalid.  With
+ * tokens = 1 the size covers both a decode of `batch` sequences and a
+ * one-token prefill.
+ */
+size_t llama_layer_workspace_size(const ll_config* cfg, int32_t batch, int32_t tokens,
+                                  int32_t s_max);
+
+/*
+ * Prefill ("Llama2架构与推理全解析" §2.1): all `tokens` new tokens of each of
+ * `batch` sequences at positions start_pos .. start_pos+tokens-1.
+ *   x        [batch, tokens, H] act_dtype, read only
+ *   y        [batch, tokens, H] act_dtype, written; must not overlap x
+ *   k_cache, v_cache  [batch, n_kv_heads, s_max, head_dim] kv_dtype: positions
+ *            < start_pos are read as they are, the new positions are written
+ *   ws       workspace of at least llama_layer_workspace_size(cfg, batch, tokens, s_max) bytes
+ * Errors: LL_ECACHE_FULL if start_pos + tokens > s_max or > max_pos.
+ */
+int llama_layer_prefill(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                        void* k_cache, void* v_cache, int32_t batch, int32_t tokens,
+                        int32_t start_pos, int32_t s_max, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * Decode ("Llama2架构与推理全解析" §2.1, §2.4): one new token per sequence.
+ *   x        [batch, H] act_dtype;  y [batch, H] act_dtype (no overlap with x)
+ *   ctx_len  DEVICE int32 [batch]: tokens already cached for each sequence; the
+ *            new token sits at position ctx_len[b], its K/V are written there and
+ *            its query attends over positions 0..ctx_len[b].  Read only: the
+ *            caller advances it (the cache owner's cur_pos += 1).
+ *   max_ctx  HOST int: an upper bound of every ctx_len[b]; sizes the launch.
+ *            Device values outside [0, max_ctx] are clamped into it (no fault,
+ *            result undefined).
+ * Errors: LL_ECACHE_FULL if max_ctx + 1 > s_max or > max_pos.
+ */
+int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                       void* k_cache, void* v_cache, const int32_t* ctx_len, int32_t batch,
+                       int32_t max_ctx, int32_t s_max, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * RoPE angle tables: cos/sin[m, i] = cos/sin(m * rope_theta^(-2i/head_dim)) for
+ * m < max_pos, i < head_dim/2, evaluated in float64 on the device and rounded
+ * to float32 ("Llama2架构与推理全解析" §1.4).  cos_out, sin_out: device float32
+ * [max_pos, head_dim/2].
+ */
+int llama_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
+                     float rope_theta, void* stream);
+
+/*
+ * Embedding lookup ("Llama2架构与推理全解析" §2.3): h[i, :] = table[ids[i], :].
+ *   table [vocab, hidden] dtype; ids DEVICE int32 [n] (clamped into [0, vocab));
+ *   h [n, hidden] dtype.
+ */
+int llama_embed(const void* table, const int32_t* ids, void* h, int32_t n, int32_t hidden,
+                int32_t vocab, int32_t dtype, void* stream);
+
+/*
+ * Output head and greedy pick ("Llama2架构与推理全解析" §2.3, §2.5):
+ * logits = RMSNorm(h; final_norm, eps) W_lm^T, ids_out[i] = argmax_v logits[i, v]
+ * with ties going to the lowest index.
+ *   final_norm [hidden], w_lm [vocab, hidden], h [n, hidden]: dtype
+ *   ids_out DEVICE int32 [n]; logits DEVICE float32 [n, vocab] (required: it is
+ *   also the scratch of the argmax)
+ */
+int llama_head_argmax(const void* final_norm, const void* w_lm, const void* h,
+                      int32_t* ids_out, float* logits, int32_t n, int32_t hidden,
+                      int32_t vocab, float eps, int32_t dtype, void* stream);
+
+/* Static description of an error code. */
+const char* llama_layer_strerror(int code);
+
+/*
+ * Kernel timing (benchmark instrumentation).  llama_layer_timer_start arms
+ * HIP-event pairs around up to max_launches future launches of kernel
+ * `kernel_id` (see llama_layer_kernel_name) on whatever stream they are
+ * enqueued; llama_layer_timer_stop waits for those events, writes the summed
+ * milliseconds and the number of timed launches, and disarms.  Not thread-safe;
+ * creates and destroys HIP events (host-side objects, no device memory).
+ */
+int llama_layer_timer_start(int32_t kernel_id, int32_t max_launches);
+int llama_layer_timer_stop(double* total_ms, int32_t* launches);
+/* Name of a kernel id, or NULL past the last one. */
+const char* llama_layer_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLAMA_LAYER_H */

@@ -1,0 +1,199 @@
+"""ctypes binding of libllama_layer.so (include/llama_layer.h).
+
+Argument marshalling only: torch tensors become device pointers, Python ints
+become C ints, the current torch stream becomes the hipStream_t.  Every step of
+the layer runs in the library's HIP kernels; there is no fallback.  The library
+is opened after torch so that it binds to the HIP runtime torch already loaded
+(one runtime per process: the stream and pointers are shared).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libllama_layer.so")
+
+LL_F32, LL_BF16, LL_F16 = 0, 1, 2
+DTYPE_CODE = {"f32": LL_F32, "bf16": LL_BF16, "f16": LL_F16,
+              torch.float32: LL_F32, torch.bfloat16: LL_BF16, torch.float16: LL_F16}
+TORCH_DTYPE = {LL_F32: torch.float32, LL_BF16: torch.bfloat16, LL_F16: torch.float16}
+
+ERRORS = {0: "LL_OK", -1: "LL_EINVAL", -2: "LL_ENULL", -3: "LL_EALIGN", -4: "LL_ECACHE_FULL",
+          -5: "LL_EWORKSPACE", -6: "LL_EHIP", -7: "LL_EUNSUPPORTED"}
+
+
+class LlamaLayerError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({llama_layer_strerror(code)})")
+
+
+class ll_config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("intermediate", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("act_dtype", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("max_pos", ctypes.c_int32)]
+
+
+class ll_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "w_q", "w_k", "w_v", "w_o", "ffn_norm", "w_gate", "w_up",
+                 "w_down", "rope_cos", "rope_sin")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Open the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m llama2_decoder_layer_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        CP = ctypes.POINTER(ll_config)
+        WP = ctypes.POINTER(ll_weights)
+        L.llama_layer_workspace_size.argtypes = [CP, I32, I32, I32]
+        L.llama_layer_workspace_size.restype = SZ
+        L.llama_layer_prefill.argtypes = [CP, WP, P, P, P, P, I32, I32, I32, I32, P, SZ, P]
+        L.llama_layer_prefill.restype = ctypes.c_int
+        L.llama_layer_decode.argtypes = [CP, WP, P, P, P, P, P, I32, I32, I32, P, SZ, P]
+        L.llama_layer_decode.restype = ctypes.c_int
+        L.llama_rope_table.argtypes = [P, P, I32, I32, F, P]
+        L.llama_rope_table.restype = ctypes.c_int
+        L.llama_embed.argtypes = [P, P, P, I32, I32, I32, I32, P]
+        L.llama_embed.restype = ctypes.c_int
+        L.llama_head_argmax.argtypes = [P, P, P, P, P, I32, I32, I32, F, I32, P]
+        L.llama_head_argmax.restype = ctypes.c_int
+        L.llama_layer_strerror.argtypes = [ctypes.c_int]
+        L.llama_layer_strerror.restype = ctypes.c_char_p
+        L.llama_layer_timer_start.argtypes = [I32, I32]
+        L.llama_layer_timer_start.restype = ctypes.c_int
+        L.llama_layer_timer_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]
+        L.llama_layer_timer_stop.restype = ctypes.c_int
+        L.llama_layer_kernel_name.argtypes = [I32]
+        L.llama_layer_kernel_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise LlamaLayerError(rc, what)
+
+
+# --------------------------------------------------------------------------
+# Structures
+# --------------------------------------------------------------------------
+
+def make_config(hidden, n_heads, n_kv_heads, head_dim, intermediate, eps, rope_theta,
+                act_dtype, kv_dtype, max_pos) -> ll_config:
+    return ll_config(hidden, n_heads, n_kv_heads, head_dim, intermediate, eps, rope_theta,
+                     DTYPE_CODE[act_dtype], DTYPE_CODE[kv_dtype], max_pos)
+
+
+class LayerWeights:
+    """Holds one layer's device tensors (keeping them alive) and their ll_weights."""
+
+    NAMES = ("attn_norm", "w_q", "w_k", "w_v", "w_o", "ffn_norm", "w_gate", "w_up", "w_down",
+             "rope_cos", "rope_sin")
+
+    def __init__(self, tensors: dict):
+        self.tensors = dict(tensors)
+        self.struct = ll_weights(*[_ptr(self.tensors[n]) for n in self.NAMES])
+
+
+# --------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+
+def llama_layer_workspace_size(cfg: ll_config, batch: int, tokens: int, s_max: int) -> int:
+    return int(lib().llama_layer_workspace_size(ctypes.byref(cfg), batch, tokens, s_max))
+
+
+def llama_layer_prefill(cfg, weights: LayerWeights, x, y, k_cache, v_cache, batch, tokens,
+                        start_pos, s_max, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    rc = lib().llama_layer_prefill(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x),
+                                   _ptr(y), _ptr(k_cache), _ptr(v_cache), batch, tokens,
+                                   start_pos, s_max, _ptr(ws), nbytes, _stream(stream))
+    _check(rc, "llama_layer_prefill")
+
+
+def llama_layer_decode(cfg, weights: LayerWeights, x, y, k_cache, v_cache, ctx_len, batch,
+                       max_ctx, s_max, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    rc = lib().llama_layer_decode(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x),
+                                  _ptr(y), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), batch,
+                                  max_ctx, s_max, _ptr(ws), nbytes, _stream(stream))
+    _check(rc, "llama_layer_decode")
+
+
+def llama_rope_table(cos, sin, max_pos, head_dim, rope_theta, stream=None) -> None:
+    _check(lib().llama_rope_table(_ptr(cos), _ptr(sin), max_pos, head_dim, rope_theta,
+                                  _stream(stream)), "llama_rope_table")
+
+
+def llama_embed(table, ids, h, n, hidden, vocab, dtype, stream=None) -> None:
+    _check(lib().llama_embed(_ptr(table), _ptr(ids), _ptr(h), n, hidden, vocab,
+                             DTYPE_CODE[dtype], _stream(stream)), "llama_embed")
+
+
+def llama_head_argmax(final_norm, w_lm, h, ids_out, logits, n, hidden, vocab, eps, dtype,
+                      stream=None) -> None:
+    _check(lib().llama_head_argmax(_ptr(final_norm), _ptr(w_lm), _ptr(h), _ptr(ids_out),
+                                   _ptr(logits), n, hidden, vocab, eps, DTYPE_CODE[dtype],
+                                   _stream(stream)), "llama_head_argmax")
+
+
+def llama_layer_strerror(code: int) -> str:
+    return lib().llama_layer_strerror(code).decode()
+
+
+def llama_layer_timer_start(kernel_id: int, max_launches: int) -> None:
+    _check(lib().llama_layer_timer_start(kernel_id, max_launches), "llama_layer_timer_start")
+
+
+def llama_layer_timer_stop() -> tuple:
+    ms = ctypes.c_double()
+    n = ctypes.c_int32()
+    _check(lib().llama_layer_timer_stop(ctypes.byref(ms), ctypes.byref(n)), "llama_layer_timer_stop")
+    return ms.value, n.value
+
+
+def llama_layer_kernel_name(kernel_id: int):
+    r = lib().llama_layer_kernel_name(kernel_id)
+    return None if r is None else r.decode()
+
+
+def kernel_id(name: str) -> int:
+    i = 0
+    while True:
+        n = llama_layer_kernel_name(i)
+        if n is None:
+            raise KeyError(name)
+        if n == name:
+            return i
+        i += 1

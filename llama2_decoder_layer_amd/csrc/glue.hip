@@ -1,0 +1,81 @@
+// Small kernels around the layer: RoPE angle tables, embedding gather and the
+// greedy pick over logits.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace ll {
+
+// cos/sin(m * theta^(-2i/hd)) in float64, rounded once to float32
+// ("Llama2架构与推理全解析" §1.4: each dimension pair turns at its own rate).
+__global__ void rope_table_kernel(float* c, float* sn, int max_pos, int hd, double theta) {
+  const int half = hd / 2;
+  const size_t total = (size_t)max_pos * half;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(idx / half);
+    const int i = (int)(idx - (size_t)m * half);
+    const double inv = pow(theta, -2.0 * (double)i / (double)hd);
+    const double ang = (double)m * inv;
+    c[idx] = (float)cos(ang);
+    sn[idx] = (float)sin(ang);
+  }
+}
+
+hipError_t launch_rope_table(float* c, float* sn, int max_pos, int hd, float theta, hipStream_t s) {
+  const size_t total = (size_t)max_pos * (hd / 2);
+  int grid = (int)((total + 255) / 256);
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, s, c, sn, max_pos, hd, (double)theta);
+  return hipGetLastError();
+}
+
+// h[i, :] = table[ids[i], :]   (ids clamped into [0, vocab)).
+__global__ void embed_kernel(const uint8_t* table, const int32_t* ids, uint8_t* h, int row_bytes,
+                             int vocab) {
+  int id = ids[blockIdx.x];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  const uint8_t* src = table + (size_t)id * row_bytes;
+  uint8_t* dst = h + (size_t)blockIdx.x * row_bytes;
+  for (int c = threadIdx.x; c < row_bytes / 16; c += blockDim.x) st16(dst + c * 16, ld16(src + c * 16));
+}
+
+hipError_t launch_embed(const void* table, const int32_t* ids, void* h, int n, int H, int vocab,
+                        int dt, hipStream_t s) {
+  const int row_bytes = H * (dt == DT_F32 ? 4 : 2);
+  hipLaunchKernelGGL(embed_kernel, dim3(n), dim3(256), 0, s, (const uint8_t*)table, ids, (uint8_t*)h,
+                     row_bytes, vocab);
+  return hipGetLastError();
+}
+
+// ids[i] = argmax_v logits[i, v]; ties go to the lowest index.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int32_t* ids, int vocab) {
+  const float* r = logits + (size_t)blockIdx.x * vocab;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int v = threadIdx.x; v < vocab; v += 256) {
+    const float x = r[v];
+    if (x > best) { best = x; bi = v; }  // strided scan: the first hit of a value is the lowest
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+  }
+  __shared__ float sb[4];
+  __shared__ int si[4];
+  if ((threadIdx.x & 63) == 0) { sb[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (sb[w] > best || (sb[w] == best && si[w] < bi)) { best = sb[w]; bi = si[w]; }
+    ids[blockIdx.x] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+hipError_t launch_argmax(const float* logits, int32_t* ids, int n, int vocab, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(n), dim3(256), 0, s, logits, ids, vocab);
+  return hipGetLastError();
+}
+
+}  // namespace ll

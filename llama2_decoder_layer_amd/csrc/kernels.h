@@ -1,0 +1,99 @@
+// Host-side launch interface between the C ABI (layer.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ll {
+
+enum Epi {
+  EPI_QKV = 0,     // RoPE on q/k, q to the workspace, k/v appended to the caches
+  EPI_RESID = 1,   // y = resid + acc
+  EPI_SWIGLU = 2,  // y = silu(acc_gate) * acc_up   (two weight matrices)
+  EPI_LOGITS = 3,  // y (float32) = acc
+};
+
+// Arguments of one projection y[m, n] = sum_k act(x)[m, k] * W[n, k].
+struct ProjArgs {
+  const void* w[3];   // row segments: [0,seg1) w[0]; [seg1,seg2) w[1]; [seg2,N) w[2]
+  int seg1, seg2;     // (EPI_SWIGLU: w[0] = gate, w[1] = up, both N rows)
+  int N, K, M;        // out features, in features, tokens in this launch
+  int tok0;           // global index of this launch's first token
+  const void* x;      // [M, K] activations (raw hidden state when `gamma` is set)
+  const void* gamma;  // RMSNorm gain [K] (fused norm) or nullptr
+  float eps;
+  const void* resid;  // [M, N] (EPI_RESID)
+  void* y;            // [M, N]
+  // EPI_QKV
+  float* q32;         // [M, nh*hd] float32, rows of this launch (decode-style attention)
+  void* q16;          // [B, nh, T, hd] in the KV-cache format (prefill attention)
+  void* kc;
+  void* vc;
+  const int32_t* ctx_len;  // decode: position of token n is ctx_len[n]; else start_pos + n%T
+  int start_pos, T, max_ctx;
+  int nh, nkv, hd, s_max, kv_dt;
+  const float* rcos;
+  const float* rsin;
+};
+
+hipError_t launch_gemv(int dt, int epi, const ProjArgs& a, hipStream_t s);
+hipError_t launch_gemm(int dt, int epi, const ProjArgs& a, hipStream_t s);
+
+// RMSNorm of `rows` rows of width H: u = x / sqrt(mean(x^2) + eps) * gamma.
+hipError_t launch_rmsnorm(int dt, const void* x, const void* gamma, void* u, int rows, int H,
+                          float eps, hipStream_t s);
+
+// Split-over-context attention for single queries.  Query n (of B*T) belongs
+// to sequence n/T at position ctx_len[n/T] (decode) or start_pos + n%T
+// (prefill); it attends over cache positions 0..pos.
+struct AttnDecodeArgs {
+  const float* q;        // [nq, nh, hd] float32
+  const void* kc;        // [B, nkv, s_max, hd]
+  const void* vc;
+  const int32_t* ctx_len;
+  int start_pos, T, max_ctx;
+  int nq, nh, nkv, hd, s_max, kv_dt, act_dt;
+  int chunk, nsplit;     // keys per split, splits per query
+  float* part_m;         // [nq, nh, nsplit]
+  float* part_l;         // [nq, nh, nsplit]
+  float* part_acc;       // [nq, nh, nsplit, hd]
+  void* o;               // [nq, nh*hd] act dtype
+};
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
+
+// Causal prefill attention with MFMA (16-bit formats).
+struct AttnPrefillArgs {
+  const void* q;   // [B, nh, T, hd] in format dt
+  const void* kc;  // [B, nkv, s_max, hd] in format dt (bf16 or f16)
+  const void* vc;
+  void* o;         // [B, T, nh*hd] in format out_dt
+  int B, T, start_pos, nh, nkv, hd, s_max, dt, out_dt;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
+
+hipError_t launch_rope_table(float* c, float* sn, int max_pos, int hd, float theta, hipStream_t s);
+hipError_t launch_embed(const void* table, const int32_t* ids, void* h, int n, int H, int vocab,
+                        int dt, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int32_t* ids, int n, int vocab, hipStream_t s);
+
+// Kernel ids for the timing hooks (order matches kernel_names in layer.hip).
+enum KernelId {
+  KID_RMSNORM = 0,
+  KID_GEMV_QKV,
+  KID_GEMV_O,
+  KID_GEMV_GATEUP,
+  KID_GEMV_DOWN,
+  KID_GEMM_QKV,
+  KID_GEMM_O,
+  KID_GEMM_GATEUP,
+  KID_GEMM_DOWN,
+  KID_ATTN_DECODE,
+  KID_ATTN_PREFILL,
+  KID_COUNT
+};
+// Records the start/stop events around a launch when that kernel is armed.
+void timer_before(int kid, hipStream_t s);
+void timer_after(int kid, hipStream_t s);
+
+}  // namespace ll

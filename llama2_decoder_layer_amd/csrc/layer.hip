@@ -1,0 +1,499 @@
+// C ABI of the decoder layer: argument validation, workspace carving and the
+// launch sequence of prefill and decode.  No allocation, no synchronisation.
+//
+// Two launch plans, chosen from the token count and format only (so the
+// workspace size is known in advance):
+//  * "token-skinny" (decode, and prefill of <= 32 tokens or float32):
+//      QKV projection with fused RMSNorm + RoPE + cache append  (gemv)
+//      split-over-context attention + log-sum-exp combine        (attn_decode)
+//      O projection + residual                                   (gemv)
+//      gate/up projection with fused RMSNorm + SwiGLU            (gemv)
+//      down projection + residual                                (gemv)
+//    Float32 layers with more than 32 tokens run this plan 32 tokens at a time.
+//  * "token-wide" (prefill of > 32 tokens in bf16/f16):
+//      RMSNorm, QKV GEMM + RoPE + cache append, causal MFMA attention,
+//      O GEMM + residual, RMSNorm, gate/up GEMM + SwiGLU, down GEMM + residual.
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+#include "llama_layer.h"
+
+namespace ll {
+
+static size_t esize(int dt) { return dt == LL_F32 ? 4 : 2; }
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// Timing hooks.
+// ---------------------------------------------------------------------------
+static const char* kernel_names[KID_COUNT] = {
+    "rmsnorm",        "gemv_qkv",    "gemv_o",    "gemv_gate_up",   "gemv_down",  "gemm_qkv",
+    "gemm_o",         "gemm_gate_up", "gemm_down", "attn_decode",   "attn_prefill"};
+
+struct Timer {
+  int kid = -1;
+  int max = 0;
+  int count = 0;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+};
+static Timer g_timer;
+
+void timer_before(int kid, hipStream_t s) {
+  if (g_timer.kid != kid || g_timer.count >= g_timer.max) return;
+  (void)hipEventRecord(g_timer.ev[2 * g_timer.count], s);
+}
+void timer_after(int kid, hipStream_t s) {
+  if (g_timer.kid != kid || g_timer.count >= g_timer.max) return;
+  (void)hipEventRecord(g_timer.ev[2 * g_timer.count + 1], s);
+  ++g_timer.count;
+}
+
+// ---------------------------------------------------------------------------
+// Validation.
+// ---------------------------------------------------------------------------
+static int check_config(const ll_config* c) {
+  if (!c) return LL_ENULL;
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->intermediate <= 0 || c->max_pos <= 0)
+    return LL_EINVAL;
+  if (c->n_heads % c->n_kv_heads) return LL_EINVAL;
+  if (c->hidden % 8 || c->intermediate % 8 || c->head_dim % 2) return LL_EINVAL;
+  if (!(c->eps > 0.f) || !(c->eps < 1.f) || !(c->rope_theta > 1.f)) return LL_EINVAL;
+  if (c->act_dtype < LL_F32 || c->act_dtype > LL_F16 || c->kv_dtype < LL_F32 || c->kv_dtype > LL_F16)
+    return LL_EINVAL;
+  if ((c->act_dtype == LL_F32) != (c->kv_dtype == LL_F32)) return LL_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return LL_EUNSUPPORTED;
+  return LL_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return LL_ENULL;
+  for (const void* p : ps)
+    if (!aligned16(p)) return LL_EALIGN;
+  return LL_OK;
+}
+
+static int check_weights(const ll_weights* w) {
+  if (!w) return LL_ENULL;
+  return check_ptrs({w->attn_norm, w->w_q, w->w_k, w->w_v, w->w_o, w->ffn_norm, w->w_gate, w->w_up,
+                     w->w_down, w->rope_cos, w->rope_sin});
+}
+
+// int32 id/length arrays and float32 logits are accessed element by element.
+static int check_ptrs4(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return LL_ENULL;
+  for (const void* p : ps)
+    if ((uintptr_t)p & 3u) return LL_EALIGN;
+  return LL_OK;
+}
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout.
+// ---------------------------------------------------------------------------
+static bool wide_plan(const ll_config* c, int64_t tokens_total, bool decode) {
+  return !decode && c->act_dtype != LL_F32 && tokens_total > 32;
+}
+
+constexpr int CHUNK_MIN = 64;
+
+struct Layout {
+  size_t q32, pm, pl, pacc, u, q16, o, h1, a, total;
+  int nsplit_max;
+};
+
+static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide) {
+  Layout L{};
+  const size_t act = esize(c->act_dtype);
+  const size_t qd = (size_t)c->n_heads * c->head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  if (wide) {
+    L.u = take(bt * c->hidden * act);
+    L.q16 = take(bt * qd * esize(c->kv_dtype));
+  } else {
+    // Token-skinny plans process at most 32 tokens at a time.
+    const int64_t g = std::min<int64_t>(bt, 32);
+    L.nsplit_max = (s_max + CHUNK_MIN - 1) / CHUNK_MIN;
+    L.q32 = take(g * qd * 4);
+    L.pm = take(g * c->n_heads * L.nsplit_max * 4);
+    L.pl = take(g * c->n_heads * L.nsplit_max * 4);
+    L.pacc = take(g * c->n_heads * L.nsplit_max * c->head_dim * 4);
+  }
+  L.o = take(bt * qd * act);
+  L.h1 = take(bt * c->hidden * act);
+  L.a = take(bt * c->intermediate * act);
+  L.total = off;
+  return L;
+}
+
+static int pick_chunk(int max_keys, int queries, int heads_groups) {
+  // Largest power-of-two chunk in [64, 512] that still gives >= 2048 workgroups.
+  int chunk = 512;
+  while (chunk > CHUNK_MIN) {
+    const int64_t wgs = (int64_t)((max_keys + chunk - 1) / chunk) * queries * heads_groups;
+    if (wgs >= 2048) break;
+    chunk >>= 1;
+  }
+  return chunk;
+}
+
+// ---------------------------------------------------------------------------
+// Launch plans.
+// ---------------------------------------------------------------------------
+#define LL_TRY(expr)                           \
+  do {                                         \
+    if ((expr) != hipSuccess) return LL_EHIP;  \
+  } while (0)
+
+static ProjArgs base_args(const ll_config* c) {
+  ProjArgs p;
+  memset(&p, 0, sizeof(p));
+  p.eps = c->eps;
+  p.nh = c->n_heads;
+  p.nkv = c->n_kv_heads;
+  p.hd = c->head_dim;
+  p.kv_dt = c->kv_dtype;
+  return p;
+}
+
+// Token-skinny plan for tokens [tok0, tok0 + m) of B*T.
+static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, void* y, void* kc,
+                      void* vc, const int32_t* ctx_len, int start_pos, int T, int max_ctx,
+                      int s_max, int64_t tok0, int m, uint8_t* ws, const Layout& L,
+                      hipStream_t s) {
+  const int dt = c->act_dtype;
+  const size_t act = esize(dt);
+  const int H = c->hidden, I = c->intermediate;
+  const int qd = c->n_heads * c->head_dim, kd = c->n_kv_heads * c->head_dim;
+  const uint8_t* xm = (const uint8_t*)x + tok0 * H * act;
+  uint8_t* ym = (uint8_t*)y + tok0 * H * act;
+  uint8_t* o = ws + L.o + tok0 * qd * act;
+  uint8_t* h1 = ws + L.h1 + tok0 * H * act;
+  uint8_t* a = ws + L.a + tok0 * I * act;
+
+  // 1. QKV + RMSNorm + RoPE + cache append.
+  ProjArgs p = base_args(c);
+  p.w[0] = w->w_q; p.w[1] = w->w_k; p.w[2] = w->w_v;
+  p.seg1 = qd; p.seg2 = qd + kd;
+  p.N = qd + 2 * kd; p.K = H; p.M = m; p.tok0 = (int)tok0;
+  p.x = xm; p.gamma = w->attn_norm;
+  p.q32 = (float*)(ws + L.q32);
+  p.kc = kc; p.vc = vc; p.ctx_len = ctx_len; p.start_pos = start_pos; p.T = T;
+  p.max_ctx = max_ctx; p.s_max = s_max; p.rcos = w->rope_cos; p.rsin = w->rope_sin;
+  timer_before(KID_GEMV_QKV, s);
+  LL_TRY(launch_gemv(dt, EPI_QKV, p, s));
+  timer_after(KID_GEMV_QKV, s);
+
+  // 2. Attention over the cache.
+  AttnDecodeArgs at;
+  memset(&at, 0, sizeof(at));
+  at.q = p.q32; at.kc = kc; at.vc = vc; at.ctx_len = ctx_len; at.start_pos = start_pos;
+  at.T = T; at.max_ctx = max_ctx; at.nq = m; at.nh = c->n_heads; at.nkv = c->n_kv_heads;
+  at.hd = c->head_dim; at.s_max = s_max; at.kv_dt = c->kv_dtype; at.act_dt = dt;
+  const int max_keys = ctx_len ? max_ctx + 1 : start_pos + T;
+  const int g = c->n_heads / c->n_kv_heads;
+  const int gc = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
+  at.chunk = pick_chunk(max_keys, m, c->n_kv_heads * (g / gc));
+  at.nsplit = (max_keys + at.chunk - 1) / at.chunk;
+  if (at.nsplit > L.nsplit_max) return LL_EWORKSPACE;
+  at.part_m = (float*)(ws + L.pm); at.part_l = (float*)(ws + L.pl);
+  at.part_acc = (float*)(ws + L.pacc); at.o = o;
+  // Query n of this launch is global token tok0 + n.  Decode: sequence tok0 + n
+  // at ctx_len[tok0 + n].  Prefill: the launch lies inside one sequence
+  // b0 = tok0 / T, its queries at positions start_pos + tok0 % T + n.
+  const size_t seq_bytes = (size_t)c->n_kv_heads * s_max * c->head_dim * esize(c->kv_dtype);
+  int64_t b0;
+  if (ctx_len) {
+    b0 = tok0;
+    at.ctx_len = ctx_len + tok0;
+    at.T = 1;
+  } else {
+    if ((tok0 % T) + m > T) return LL_EINVAL;
+    b0 = tok0 / T;
+    at.start_pos = start_pos + (int)(tok0 % T);
+    at.T = m;
+  }
+  at.kc = (const uint8_t*)kc + b0 * seq_bytes;
+  at.vc = (const uint8_t*)vc + b0 * seq_bytes;
+  timer_before(KID_ATTN_DECODE, s);
+  LL_TRY(launch_attn_decode(at, s));
+  timer_after(KID_ATTN_DECODE, s);
+
+  // 3. O projection + residual.
+  ProjArgs po = base_args(c);
+  po.w[0] = w->w_o; po.seg1 = po.seg2 = H;
+  po.N = H; po.K = qd; po.M = m; po.x = o; po.resid = xm; po.y = h1;
+  timer_before(KID_GEMV_O, s);
+  LL_TRY(launch_gemv(dt, EPI_RESID, po, s));
+  timer_after(KID_GEMV_O, s);
+
+  // 4. gate/up + RMSNorm + SwiGLU.
+  ProjArgs pg = base_args(c);
+  pg.w[0] = w->w_gate; pg.w[1] = w->w_up;
+  pg.N = I; pg.K = H; pg.M = m; pg.x = h1; pg.gamma = w->ffn_norm; pg.y = a;
+  timer_before(KID_GEMV_GATEUP, s);
+  LL_TRY(launch_gemv(dt, EPI_SWIGLU, pg, s));
+  timer_after(KID_GEMV_GATEUP, s);
+
+  // 5. down + residual.
+  ProjArgs pd = base_args(c);
+  pd.w[0] = w->w_down; pd.seg1 = pd.seg2 = H;
+  pd.N = H; pd.K = I; pd.M = m; pd.x = a; pd.resid = h1; pd.y = ym;
+  timer_before(KID_GEMV_DOWN, s);
+  LL_TRY(launch_gemv(dt, EPI_RESID, pd, s));
+  timer_after(KID_GEMV_DOWN, s);
+  return LL_OK;
+}
+
+static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void* y, void* kc,
+                    void* vc, int B, int T, int start_pos, int s_max, uint8_t* ws,
+                    const Layout& L, hipStream_t s) {
+  const int dt = c->act_dtype;
+  const int H = c->hidden, I = c->intermediate;
+  const int qd = c->n_heads * c->head_dim, kd = c->n_kv_heads * c->head_dim;
+  const int M = B * T;
+  void* u = ws + L.u;
+
+  timer_before(KID_RMSNORM, s);
+  LL_TRY(launch_rmsnorm(dt, x, w->attn_norm, u, M, H, c->eps, s));
+  timer_after(KID_RMSNORM, s);
+
+  ProjArgs p = base_args(c);
+  p.w[0] = w->w_q; p.w[1] = w->w_k; p.w[2] = w->w_v;
+  p.seg1 = qd; p.seg2 = qd + kd;
+  p.N = qd + 2 * kd; p.K = H; p.M = M; p.x = u;
+  p.q16 = ws + L.q16; p.kc = kc; p.vc = vc; p.start_pos = start_pos; p.T = T;
+  p.s_max = s_max; p.rcos = w->rope_cos; p.rsin = w->rope_sin;
+  timer_before(KID_GEMM_QKV, s);
+  LL_TRY(launch_gemm(dt, EPI_QKV, p, s));
+  timer_after(KID_GEMM_QKV, s);
+
+  AttnPrefillArgs ap;
+  ap.q = ws + L.q16; ap.kc = kc; ap.vc = vc; ap.o = ws + L.o;
+  ap.B = B; ap.T = T; ap.start_pos = start_pos; ap.nh = c->n_heads; ap.nkv = c->n_kv_heads;
+  ap.hd = c->head_dim; ap.s_max = s_max; ap.dt = c->kv_dtype; ap.out_dt = dt;
+  timer_before(KID_ATTN_PREFILL, s);
+  LL_TRY(launch_attn_prefill(ap, s));
+  timer_after(KID_ATTN_PREFILL, s);
+
+  ProjArgs po = base_args(c);
+  po.w[0] = w->w_o; po.seg1 = po.seg2 = H;
+  po.N = H; po.K = qd; po.M = M; po.x = ws + L.o; po.resid = x; po.y = ws + L.h1;
+  timer_before(KID_GEMM_O, s);
+  LL_TRY(launch_gemm(dt, EPI_RESID, po, s));
+  timer_after(KID_GEMM_O, s);
+
+  timer_before(KID_RMSNORM, s);
+  LL_TRY(launch_rmsnorm(dt, ws + L.h1, w->ffn_norm, u, M, H, c->eps, s));
+  timer_after(KID_RMSNORM, s);
+
+  ProjArgs pg = base_args(c);
+  pg.w[0] = w->w_gate; pg.w[1] = w->w_up;
+  pg.N = I; pg.K = H; pg.M = M; pg.x = u; pg.y = ws + L.a;
+  timer_before(KID_GEMM_GATEUP, s);
+  LL_TRY(launch_gemm(dt, EPI_SWIGLU, pg, s));
+  timer_after(KID_GEMM_GATEUP, s);
+
+  ProjArgs pd = base_args(c);
+  pd.w[0] = w->w_down; pd.seg1 = pd.seg2 = H;
+  pd.N = H; pd.K = I; pd.M = M; pd.x = ws + L.a; pd.resid = ws + L.h1; pd.y = y;
+  timer_before(KID_GEMM_DOWN, s);
+  LL_TRY(launch_gemm(dt, EPI_RESID, pd, s));
+  timer_after(KID_GEMM_DOWN, s);
+  return LL_OK;
+}
+
+}  // namespace ll
+
+using namespace ll;
+
+extern "C" {
+
+size_t llama_layer_workspace_size(const ll_config* cfg, int32_t batch, int32_t tokens, int32_t s_max) {
+  if (check_config(cfg) != LL_OK || batch <= 0 || tokens <= 0 || s_max <= 0) return 0;
+  const int64_t bt = (int64_t)batch * tokens;
+  size_t need = layout(cfg, bt, s_max, wide_plan(cfg, bt, false)).total;
+  // tokens == 1 also sizes a decode of `batch` sequences (the token-skinny plan).
+  if (tokens == 1) need = std::max(need, layout(cfg, bt, s_max, false).total);
+  return need;
+}
+
+int llama_layer_prefill(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                        void* k_cache, void* v_cache, int32_t batch, int32_t tokens,
+                        int32_t start_pos, int32_t s_max, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if ((rc = check_ptrs({x, y, k_cache, v_cache}))) return rc;
+  if (batch <= 0 || tokens <= 0 || start_pos < 0 || s_max <= 0) return LL_EINVAL;
+  if ((int64_t)start_pos + tokens > s_max || (int64_t)start_pos + tokens > cfg->max_pos)
+    return LL_ECACHE_FULL;
+  const int64_t bt = (int64_t)batch * tokens;
+  const size_t act = esize(cfg->act_dtype);
+  if (overlap(x, bt * cfg->hidden * act, y, bt * cfg->hidden * act)) return LL_EINVAL;
+  const bool wide = wide_plan(cfg, bt, false);
+  const Layout L = layout(cfg, bt, s_max, wide);
+  if (!ws) return LL_EWORKSPACE;
+  if (!aligned16(ws)) return LL_EALIGN;
+  if (ws_bytes < L.total) return LL_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (wide)
+    return run_wide(cfg, w, x, y, k_cache, v_cache, batch, tokens, start_pos, s_max,
+                    (uint8_t*)ws, L, s);
+  // Token-skinny prefill: groups of <= 32 tokens that never straddle sequences.
+  for (int b = 0; b < batch; ++b) {
+    for (int t0 = 0; t0 < tokens; t0 += 32) {
+      const int m = std::min(32, tokens - t0);
+      rc = run_skinny(cfg, w, x, y, k_cache, v_cache, nullptr, start_pos, tokens, 0, s_max,
+                      (int64_t)b * tokens + t0, m, (uint8_t*)ws, L, s);
+      if (rc) return rc;
+    }
+  }
+  return LL_OK;
+}
+
+int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                       void* k_cache, void* v_cache, const int32_t* ctx_len, int32_t batch,
+                       int32_t max_ctx, int32_t s_max, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if ((rc = check_ptrs({x, y, k_cache, v_cache}))) return rc;
+  if ((rc = check_ptrs4({ctx_len}))) return rc;
+  if (batch <= 0 || max_ctx < 0 || s_max <= 0) return LL_EINVAL;
+  if ((int64_t)max_ctx + 1 > s_max || (int64_t)max_ctx + 1 > cfg->max_pos) return LL_ECACHE_FULL;
+  const size_t act = esize(cfg->act_dtype);
+  if (overlap(x, (size_t)batch * cfg->hidden * act, y, (size_t)batch * cfg->hidden * act))
+    return LL_EINVAL;
+  const Layout L = layout(cfg, batch, s_max, false);
+  if (!ws) return LL_EWORKSPACE;
+  if (!aligned16(ws)) return LL_EALIGN;
+  if (ws_bytes < L.total) return LL_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  for (int b0 = 0; b0 < batch; b0 += 32) {
+    const int m = std::min(32, batch - b0);
+    rc = run_skinny(cfg, w, x, y, k_cache, v_cache, ctx_len, 0, 1, max_ctx, s_max, b0, m,
+                    (uint8_t*)ws, L, s);
+    if (rc) return rc;
+  }
+  return LL_OK;
+}
+
+int llama_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
+                     float rope_theta, void* stream) {
+  if (!cos_out || !sin_out) return LL_ENULL;
+  if (max_pos <= 0 || head_dim <= 0 || head_dim % 2 || !(rope_theta > 1.f)) return LL_EINVAL;
+  (void)hipGetLastError();
+  if (launch_rope_table(cos_out, sin_out, max_pos, head_dim, rope_theta, (hipStream_t)stream) != hipSuccess)
+    return LL_EHIP;
+  return LL_OK;
+}
+
+int llama_embed(const void* table, const int32_t* ids, void* h, int32_t n, int32_t hidden,
+                int32_t vocab, int32_t dtype, void* stream) {
+  int rc = check_ptrs({table, h});
+  if (rc) return rc;
+  if ((rc = check_ptrs4({ids}))) return rc;
+  if (n <= 0 || hidden <= 0 || hidden % 8 || vocab <= 0 || dtype < LL_F32 || dtype > LL_F16)
+    return LL_EINVAL;
+  (void)hipGetLastError();
+  if (launch_embed(table, ids, h, n, hidden, vocab, dtype, (hipStream_t)stream) != hipSuccess)
+    return LL_EHIP;
+  return LL_OK;
+}
+
+int llama_head_argmax(const void* final_norm, const void* w_lm, const void* h, int32_t* ids_out,
+                      float* logits, int32_t n, int32_t hidden, int32_t vocab, float eps,
+                      int32_t dtype, void* stream) {
+  int rc = check_ptrs({final_norm, w_lm, h});
+  if (rc) return rc;
+  if ((rc = check_ptrs4({ids_out, logits}))) return rc;
+  if (n <= 0 || hidden <= 0 || hidden % 8 || vocab <= 0 || dtype < LL_F32 || dtype > LL_F16 ||
+      !(eps > 0.f))
+    return LL_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const size_t esz = esize(dtype);
+  for (int r0 = 0; r0 < n; r0 += 32) {
+    ProjArgs p;
+    memset(&p, 0, sizeof(p));
+    p.w[0] = w_lm; p.seg1 = p.seg2 = vocab;
+    p.N = vocab; p.K = hidden; p.M = std::min(32, n - r0);
+    p.x = (const uint8_t*)h + (size_t)r0 * hidden * esz;
+    p.gamma = final_norm; p.eps = eps;
+    p.y = logits + (size_t)r0 * vocab;
+    if (launch_gemv(dtype, EPI_LOGITS, p, s) != hipSuccess) return LL_EHIP;
+  }
+  if (launch_argmax(logits, ids_out, n, vocab, s) != hipSuccess) return LL_EHIP;
+  return LL_OK;
+}
+
+const char* llama_layer_strerror(int code) {
+  switch (code) {
+    case LL_OK: return "ok";
+    case LL_EINVAL: return "invalid configuration or size";
+    case LL_ENULL: return "a required pointer is NULL";
+    case LL_EALIGN: return "a pointer is not 16-byte aligned";
+    case LL_ECACHE_FULL: return "positions would run past the KV-cache capacity or RoPE table";
+    case LL_EWORKSPACE: return "workspace missing or too small";
+    case LL_EHIP: return "HIP launch error";
+    case LL_EUNSUPPORTED: return "configuration not supported (head_dim must be 64 or 128)";
+  }
+  return "unknown error";
+}
+
+int llama_layer_timer_start(int32_t kernel_id, int32_t max_launches) {
+  if (kernel_id < 0 || kernel_id >= KID_COUNT || max_launches <= 0) return LL_EINVAL;
+  for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
+  g_timer.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto& e : g_timer.ev)
+    if (hipEventCreate(&e) != hipSuccess) return LL_EHIP;
+  g_timer.kid = kernel_id;
+  g_timer.max = max_launches;
+  g_timer.count = 0;
+  return LL_OK;
+}
+
+int llama_layer_timer_stop(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return LL_ENULL;
+  double tot = 0.0;
+  int rc = LL_OK;
+  for (int i = 0; i < g_timer.count; ++i) {
+    if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess) { rc = LL_EHIP; break; }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess) {
+      rc = LL_EHIP;
+      break;
+    }
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = g_timer.count;
+  for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.kid = -1;
+  g_timer.max = g_timer.count = 0;
+  return rc;
+}
+
+const char* llama_layer_kernel_name(int32_t kernel_id) {
+  if (kernel_id < 0 || kernel_id >= KID_COUNT) return nullptr;
+  return kernel_names[kernel_id];
+}
+
+}  // extern "C"

@@ -15,10 +15,13 @@ Recipes (the workloads the pages describe, made synthetic):
     that are already rotated;
   * batched-decode context lengths ~ U{lo .. hi} inclusive;
   * prompt ids ~ U{0 .. vocab-1}.
-Seeds: weights of workload k use PCG64(1000 + k), inputs PCG64(2000 + k).
+Seeds: weights of workload k descend from SeedSequence(1000 + k), inputs from
+SeedSequence(2000 + k) (one child per tensor, one grandchild per 4 Mi elements).
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -98,7 +101,7 @@ class Workload:
     """One synthetic workload: a layer shape, dtypes, a phase and its sizes."""
 
     name: str
-    index: int                 # seed index k: weights PCG64(1000+k), inputs PCG64(2000+k)
+    index: int                 # seed index k: weights 1000+k, inputs 2000+k
     shape: Shape
     act_dtype: str
     kv_dtype: str
@@ -134,9 +137,18 @@ WORKLOADS = {
 # --------------------------------------------------------------------------
 # Draws
 # --------------------------------------------------------------------------
+# Every tensor gets its own child of the workload's SeedSequence, and every
+# 4 Mi-element chunk of it a grandchild, so large tensors are drawn by a thread
+# pool and the values do not depend on the number of threads.
 
 WEIGHT_STD = 0.02
 LAYER_TENSORS = ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")
+CHUNK = 1 << 22
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16}
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 def layer_tensor_shapes(s: Shape) -> dict:
@@ -145,84 +157,105 @@ def layer_tensor_shapes(s: Shape) -> dict:
             "w_o": (H, nh * hd), "w_gate": (I, H), "w_up": (I, H), "w_down": (H, I)}
 
 
-def normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
-    a = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        a *= np.float32(std)
-    return a
+def normal(ss: np.random.SeedSequence, shape, std: float = 1.0, dtype: str = "f32") -> np.ndarray:
+    """N(0, std^2) drawn in float32 and rounded to `dtype` storage."""
+    out = np.empty(shape, dtype=STORAGE[dtype])
+    flat = out.reshape(-1)
+    n = flat.size
+    nch = max(1, (n + CHUNK - 1) // CHUNK)
+    kids = ss.spawn(nch)
+
+    def work(i):
+        lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+        a = np.random.Generator(np.random.PCG64(kids[i])).standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            a *= np.float32(std)
+        flat[lo:hi] = to_storage(a, dtype)
+
+    if nch == 1:
+        work(0)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=_workers()) as ex:
+            list(ex.map(work, range(nch)))
+    return out
 
 
-def draw_layer(rng: np.random.Generator, s: Shape, dtype: str) -> dict:
+def draw_layer(ss: np.random.SeedSequence, s: Shape, dtype: str) -> dict:
     """One layer's weights in storage form; gains are ones."""
-    out = {}
-    for name, shp in layer_tensor_shapes(s).items():
-        out[name] = to_storage(normal(rng, shp, WEIGHT_STD), dtype)
+    shapes = layer_tensor_shapes(s)
+    kids = ss.spawn(len(LAYER_TENSORS))
+    out = {name: normal(kid, shapes[name], WEIGHT_STD, dtype)
+           for name, kid in zip(LAYER_TENSORS, kids)}
     ones = np.ones(s.hidden, dtype=np.float32)
     out["attn_norm"] = to_storage(ones, dtype)
     out["ffn_norm"] = to_storage(ones, dtype)
     return out
 
 
-def weights_rng(k: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(1000 + k))
+def weights_seed(k: int) -> np.random.SeedSequence:
+    return np.random.SeedSequence(1000 + k)
 
 
-def inputs_rng(k: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(2000 + k))
+def inputs_seed(k: int) -> np.random.SeedSequence:
+    return np.random.SeedSequence(2000 + k)
 
 
 def draw_stack(w: Workload) -> dict:
-    """Tiny/large stack: layers, embedding table, final gain, LM head, prompt."""
-    rng = weights_rng(w.index)
-    layers = [draw_layer(rng, w.shape, w.act_dtype) for _ in range(w.n_layers)]
-    embed = to_storage(normal(rng, (w.vocab, w.shape.hidden), WEIGHT_STD), w.act_dtype)
-    w_lm = to_storage(normal(rng, (w.vocab, w.shape.hidden), WEIGHT_STD), w.act_dtype)
+    """Stack: layers, embedding table, final gain, LM head and the prompt."""
+    ss = weights_seed(w.index)
+    kids = ss.spawn(w.n_layers + 2)
+    layers = [draw_layer(kids[i], w.shape, w.act_dtype) for i in range(w.n_layers)]
+    embed = normal(kids[w.n_layers], (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype)
+    w_lm = normal(kids[w.n_layers + 1], (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype)
     final_norm = to_storage(np.ones(w.shape.hidden, np.float32), w.act_dtype)
-    prompt = inputs_rng(w.index).integers(0, w.vocab, size=w.prompt, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(inputs_seed(w.index)))
+    prompt = rng.integers(0, w.vocab, size=w.prompt, dtype=np.int64)
     return dict(layers=layers, embed=embed, w_lm=w_lm, final_norm=final_norm,
                 prompt=prompt.astype(np.int32))
 
 
-def draw_decode_inputs(rng: np.random.Generator, s: Shape, batch: int, s_max: int,
+def draw_decode_inputs(ss: np.random.SeedSequence, s: Shape, batch: int, s_max: int,
                        act_dtype: str, kv_dtype: str, ctx=None, ctx_range=None) -> dict:
     """Hidden states x[B, H], per-sequence lengths and pre-filled caches."""
+    k_len, k_x, k_k, k_v = ss.spawn(4)
     if ctx_range:
         lo, hi = ctx_range
+        rng = np.random.Generator(np.random.PCG64(k_len))
         ctx_len = rng.integers(lo, hi + 1, size=batch, dtype=np.int64).astype(np.int32)
     else:
         ctx_len = np.full(batch, ctx, dtype=np.int32)
-    x = to_storage(normal(rng, (batch, s.hidden)), act_dtype)
+    x = normal(k_x, (batch, s.hidden), 1.0, act_dtype)
     cshape = (batch, s.n_kv_heads, s_max, s.head_dim)
-    k_cache = to_storage(normal(rng, cshape), kv_dtype)
-    v_cache = to_storage(normal(rng, cshape), kv_dtype)
-    return dict(x=x, ctx_len=ctx_len, k_cache=k_cache, v_cache=v_cache)
+    return dict(x=x, ctx_len=ctx_len, k_cache=normal(k_k, cshape, 1.0, kv_dtype),
+                v_cache=normal(k_v, cshape, 1.0, kv_dtype))
 
 
-def draw_prefill_inputs(rng: np.random.Generator, s: Shape, batch: int, tokens: int,
+def draw_prefill_inputs(ss: np.random.SeedSequence, s: Shape, batch: int, tokens: int,
                         s_max: int, act_dtype: str, kv_dtype: str, start_pos: int = 0) -> dict:
-    """Hidden states x[B, T, H]; caches pre-filled with N(0,1) before start_pos
-    (zeros elsewhere)."""
-    x = to_storage(normal(rng, (batch, tokens, s.hidden)), act_dtype)
+    """Hidden states x[B, T, H]; caches hold N(0,1) at positions < start_pos and
+    zeros elsewhere."""
+    k_x, k_k, k_v = ss.spawn(3)
+    x = normal(k_x, (batch, tokens, s.hidden), 1.0, act_dtype)
     cshape = (batch, s.n_kv_heads, s_max, s.head_dim)
-    kc = np.zeros(cshape, dtype=np.float32)
-    vc = np.zeros(cshape, dtype=np.float32)
+    kc = np.zeros(cshape, dtype=STORAGE[kv_dtype])
+    vc = np.zeros(cshape, dtype=STORAGE[kv_dtype])
     if start_pos:
-        kc[:, :, :start_pos] = normal(rng, (batch, s.n_kv_heads, start_pos, s.head_dim))
-        vc[:, :, :start_pos] = normal(rng, (batch, s.n_kv_heads, start_pos, s.head_dim))
-    return dict(x=x, k_cache=to_storage(kc, kv_dtype), v_cache=to_storage(vc, kv_dtype),
-                start_pos=start_pos)
+        pshape = (batch, s.n_kv_heads, start_pos, s.head_dim)
+        kc[:, :, :start_pos] = normal(k_k, pshape, 1.0, kv_dtype)
+        vc[:, :, :start_pos] = normal(k_v, pshape, 1.0, kv_dtype)
+    return dict(x=x, k_cache=kc, v_cache=vc, start_pos=start_pos)
 
 
 def workload_layer_and_inputs(name: str) -> tuple:
     """(weights, inputs) of a single-layer workload, in storage form."""
     w = WORKLOADS[name]
-    weights = draw_layer(weights_rng(w.index), w.shape, w.act_dtype)
-    rng = inputs_rng(w.index)
+    weights = draw_layer(weights_seed(w.index), w.shape, w.act_dtype)
+    ss = inputs_seed(w.index)
     if w.phase == "decode":
-        inputs = draw_decode_inputs(rng, w.shape, w.batch, w.s_max, w.act_dtype, w.kv_dtype,
+        inputs = draw_decode_inputs(ss, w.shape, w.batch, w.s_max, w.act_dtype, w.kv_dtype,
                                     ctx=w.ctx, ctx_range=w.ctx_range)
     elif w.phase == "prefill":
-        inputs = draw_prefill_inputs(rng, w.shape, w.batch, w.tokens, w.s_max,
+        inputs = draw_prefill_inputs(ss, w.shape, w.batch, w.tokens, w.s_max,
                                      w.act_dtype, w.kv_dtype)
     else:
         raise ValueError(f"{name} is not a single-layer workload")

@@ -1,0 +1,174 @@
+"""The C ABI on the host: the library loads, exports every declared entry point,
+and rejects bad arguments with the documented codes before touching the GPU
+(every call below fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from llama2_decoder_layer_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llama_layer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(llama_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "llama_layer_prefill" in names and "llama_layer_decode" in names
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_one_hip_runtime_in_process():
+    B.lib()
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {m.split()[-1] for m in maps if "libamdhip64" in m}
+    assert len(hip) == 1, hip
+
+
+def test_strerror():
+    assert B.llama_layer_strerror(0) == "ok"
+    for code in range(-7, 0):
+        assert B.llama_layer_strerror(code) != "unknown error"
+    assert B.llama_layer_strerror(-99) == "unknown error"
+
+
+def test_kernel_names():
+    names = []
+    i = 0
+    while B.llama_layer_kernel_name(i) is not None:
+        names.append(B.llama_layer_kernel_name(i))
+        i += 1
+    assert {"gemv_qkv", "gemv_gate_up", "gemm_qkv", "attn_decode", "attn_prefill"} <= set(names)
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call here fails validation first
+
+
+def cfg(**kw):
+    base = dict(hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=688, eps=1e-5,
+                rope_theta=1e4, act_dtype="bf16", kv_dtype="bf16", max_pos=64)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def weights(**kw):
+    ptrs = {n: FAKE + 256 * i for i, n in enumerate(B.LayerWeights.NAMES)}
+    ptrs.update(kw)
+    w = B.LayerWeights.__new__(B.LayerWeights)
+    w.tensors = {}
+    w.struct = B.ll_weights(*[ptrs[n] for n in B.LayerWeights.NAMES])
+    return w
+
+
+def prefill_rc(c, w=None, x=FAKE + 0x100000, y=FAKE + 0x200000, kc=FAKE + 0x300000,
+               vc=FAKE + 0x400000, batch=1, tokens=8, start_pos=0, s_max=32, ws=FAKE + 0x500000,
+               ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 1  # too small: the last check, reached only if everything else passes
+    w = w or weights()
+    return B.lib().llama_layer_prefill(ctypes.byref(c), ctypes.byref(w.struct), x, y, kc, vc,
+                                       batch, tokens, start_pos, s_max, ws, ws_bytes, None)
+
+
+def decode_rc(c, w=None, x=FAKE + 0x100000, y=FAKE + 0x200000, kc=FAKE + 0x300000,
+              vc=FAKE + 0x400000, ctx=FAKE + 0x600000, batch=2, max_ctx=10, s_max=32,
+              ws=FAKE + 0x500000, ws_bytes=1):
+    w = w or weights()
+    return B.lib().llama_layer_decode(ctypes.byref(c), ctypes.byref(w.struct), x, y, kc, vc, ctx,
+                                      batch, max_ctx, s_max, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n_kv_heads=3), -1),          # n_heads % n_kv_heads != 0
+    (dict(hidden=250), -1),            # hidden not a multiple of 8
+    (dict(intermediate=690), -1),
+    (dict(head_dim=96), -7),           # unsupported head_dim
+    (dict(head_dim=63), -1),           # odd head_dim
+    (dict(eps=0.0), -1),
+    (dict(rope_theta=1.0), -1),
+    (dict(act_dtype="f32", kv_dtype="bf16"), -1),
+    (dict(act_dtype="bf16", kv_dtype="f32"), -1),
+    (dict(max_pos=0), -1),
+])
+def test_bad_config(bad, code):
+    c = cfg(**bad)
+    assert prefill_rc(c) == code
+    assert decode_rc(c) == code
+    assert B.llama_layer_workspace_size(c, 1, 8, 32) == 0
+
+
+def test_null_and_alignment():
+    c = cfg()
+    assert prefill_rc(c, x=None) == -2
+    assert prefill_rc(c, w=weights(w_o=None)) == -2
+    assert prefill_rc(c, w=weights(rope_cos=None)) == -2
+    assert prefill_rc(c, y=FAKE + 0x200008) == -3
+    assert prefill_rc(c, w=weights(w_down=FAKE + 4)) == -3
+    assert decode_rc(c, ctx=None) == -2
+    assert decode_rc(c, ctx=FAKE + 0x600002) == -3
+    assert decode_rc(c, ctx=FAKE + 0x600004) == -5   # 4-byte aligned lengths are fine
+    assert B.lib().llama_layer_prefill(None, ctypes.byref(weights().struct), FAKE, FAKE, FAKE,
+                                       FAKE, 1, 1, 0, 8, FAKE, 1, None) == -2
+
+
+def test_sizes_and_cache_capacity():
+    c = cfg()
+    assert prefill_rc(c, batch=0) == -1
+    assert prefill_rc(c, tokens=0) == -1
+    assert prefill_rc(c, start_pos=-1) == -1
+    assert prefill_rc(c, start_pos=30, tokens=3, s_max=32) == -4
+    assert prefill_rc(c, start_pos=29, tokens=3, s_max=32) == -5   # fits: workspace is next
+    assert prefill_rc(cfg(max_pos=16), tokens=17, s_max=32) == -4  # past the RoPE table
+    assert decode_rc(c, max_ctx=32, s_max=32) == -4   # the new token would sit at 32
+    assert decode_rc(c, max_ctx=31, s_max=32) == -5
+    assert decode_rc(cfg(max_pos=20), max_ctx=20, s_max=32) == -4
+    assert decode_rc(c, batch=0) == -1
+    assert decode_rc(c, max_ctx=-1) == -1
+
+
+def test_overlap_and_workspace():
+    c = cfg()
+    x = FAKE + 0x100000
+    assert prefill_rc(c, x=x, y=x + 16) == -1          # y overlaps x
+    need = B.llama_layer_workspace_size(c, 1, 8, 32)
+    assert need > 0
+    assert prefill_rc(c, ws=None) == -5
+    assert prefill_rc(c, ws=FAKE + 0x500008) == -3
+    assert prefill_rc(c, ws_bytes=need - 1) == -5
+    dneed = B.llama_layer_workspace_size(c, 2, 1, 32)
+    assert decode_rc(c, ws_bytes=dneed - 1) == -5
+
+
+def test_workspace_grows_with_work():
+    c = cfg()
+    assert B.llama_layer_workspace_size(c, 1, 64, 128) > B.llama_layer_workspace_size(c, 1, 8, 128)
+    assert B.llama_layer_workspace_size(c, 1, 1, 4096) > B.llama_layer_workspace_size(c, 1, 1, 64)
+
+
+def test_glue_validation():
+    L = B.lib()
+    assert L.llama_rope_table(None, FAKE, 8, 64, 1e4, None) == -2
+    assert L.llama_rope_table(FAKE, FAKE, 8, 63, 1e4, None) == -1
+    assert L.llama_rope_table(FAKE, FAKE, 0, 64, 1e4, None) == -1
+    assert L.llama_embed(FAKE, FAKE, FAKE, 0, 256, 512, 1, None) == -1
+    assert L.llama_embed(FAKE, FAKE + 2, FAKE, 1, 256, 512, 1, None) == -3
+    assert L.llama_embed(FAKE, FAKE, FAKE, 1, 256, 512, 7, None) == -1
+    assert L.llama_head_argmax(FAKE, FAKE, FAKE, FAKE, None, 1, 256, 512, 1e-5, 1, None) == -2
+    assert L.llama_head_argmax(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 256, 512, 0.0, 1, None) == -1
+
+
+def test_timer_validation():
+    L = B.lib()
+    assert L.llama_layer_timer_start(-1, 4) == -1
+    assert L.llama_layer_timer_start(0, 0) == -1

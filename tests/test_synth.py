@@ -25,8 +25,8 @@ def test_f16_rounding_matches_torch():
 
 
 def test_draws_are_seeded():
-    a = S.draw_layer(S.weights_rng(7), S.TINY, "bf16")
-    b = S.draw_layer(S.weights_rng(7), S.TINY, "bf16")
+    a = S.draw_layer(S.weights_seed(7), S.TINY, "bf16")
+    b = S.draw_layer(S.weights_seed(7), S.TINY, "bf16")
     for k in a:
         assert np.array_equal(a[k], b[k])
     assert a["w_q"].shape == (S.TINY.n_heads * S.TINY.head_dim, S.TINY.hidden)
@@ -48,6 +48,14 @@ def test_workload_shapes_follow_size_table():
 
 def test_ragged_lengths_in_range():
     w = S.WORKLOADS["decode_70b_b32_ragged"]
-    d = S.draw_decode_inputs(S.inputs_rng(w.index), S.Shape(64, 4, 2, 16, 32), w.batch, 8,
+    d = S.draw_decode_inputs(S.inputs_seed(w.index), S.Shape(64, 4, 2, 16, 32), w.batch, 8,
                              "bf16", "f16", ctx_range=w.ctx_range)
     assert d["ctx_len"].min() >= 512 and d["ctx_len"].max() <= 4096 and len(set(d["ctx_len"])) > 10
+
+
+def test_chunked_draw_independent_of_threads(monkeypatch):
+    a = S.normal(np.random.SeedSequence(3), (S.CHUNK * 2 + 17,), 0.5, "bf16")
+    monkeypatch.setattr(S, "_workers", lambda: 1)
+    b = S.normal(np.random.SeedSequence(3), (S.CHUNK * 2 + 17,), 0.5, "bf16")
+    assert np.array_equal(a, b)
+    assert abs(S.to_f64(a, "bf16").std() - 0.5) < 1e-3
