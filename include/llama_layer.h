@@ -161,6 +161,8 @@ int llama_embed(const void* table, const int32_t* ids, void* h, int32_t n, int32
  *   final_norm [hidden], w_lm [vocab, hidden], h [n, hidden]: dtype
  *   ids_out DEVICE int32 [n]; logits DEVICE float32 [n, vocab] (required: it is
  *   also the scratch of the argmax)
+ * Errors: LL_EUNSUPPORTED if one row of h does not fit the projection's 48 KB
+ * LDS stage (hidden > 24576 for 16-bit formats, > 12288 for float32).
  */
 int llama_head_argmax(const void* final_norm, const void* w_lm, const void* h,
                       int32_t* ids_out, float* logits, int32_t n, int32_t hidden,

@@ -7,121 +7,40 @@
 // cross-lane shuffles.  Lane l of a wave reads 64 contiguous bytes of weight
 // row l%16 per k-block; the four lane groups l/16 cover 256 contiguous bytes,
 // so each row segment is fetched whole.  The waves of a workgroup split K and
-// meet in LDS.
+// meet in LDS.  Weight blocks stream through a register ring PF blocks ahead
+// of the one being multiplied, so every wave keeps (PF+1) x 4 KB in flight.
 //
-// Fusions: the attention / FFN RMSNorm is folded in (each lane accumulates
-// sum x^2 of the slice it loads; the gain multiplies the B operand; 1/rms
-// scales the result), and the epilogue does RoPE + the KV-cache append (QKV),
-// the residual add (O, down), SwiGLU (gate/up) or float32 logits (LM head).
+// Three variants:
+//  * gemv_row (1-4 tokens): each wave owns a few rows over the full K; see below.
+//  * gemv_lds: the activations of the M tokens (M*K*size <= 48 KB) are staged
+//    once per workgroup in LDS.  With a fused RMSNorm the staging pass also
+//    multiplies by the gain and accumulates sum x^2, so 1/rms is known before
+//    the weight loop and scales the results in the epilogue.
+//  * gemv_glb: larger token counts; activation chunks come from global memory
+//    (L2) one block ahead of use.  A fused norm is not available here: the
+//    host normalises first.
+// Epilogues: RoPE + KV-cache append (QKV), residual add (O, down), SwiGLU
+// (gate/up, two weight matrices) or float32 logits (LM head).
+#include <type_traits>
+
 #include "common.cuh"
 #include "epilogue.cuh"
 
 namespace ll {
 
-template <int DT, int EPI, bool NORM, int CT, int NW>
-__global__ __launch_bounds__(NW * 64) void gemv_kernel(ProjArgs a) {
+constexpr int GEMV_LDS_BYTES = 48 * 1024;  // + static LDS stays within 64 KB
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Cross-wave reduction of the accumulators and the epilogue (wave 0).
+template <int DT, int EPI, int NA, int CT, int NW>
+__device__ __forceinline__ void gemv_finish(const ProjArgs& a, f32x4 (&acc)[NA][CT],
+                                            const float* scale_tok, int row0) {
   typedef typename Elt<DT>::T T;
-  constexpr int E = Elt<DT>::PER16;   // elements per 16-byte chunk
-  constexpr int KB = 16 * E;          // k per block: 4 lane groups x 4 chunks
-  constexpr int NA = (EPI == EPI_SWIGLU) ? 2 : 1;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  const int kg = lane >> 4;
-  const int K = a.K;
-  const int row0 = blockIdx.x * 16;
-
-  // Weight rows of this lane (rows past N read row 0; their results are dropped).
-  const int f_lane = row0 + r16;
-  const int f_safe = f_lane < a.N ? f_lane : 0;
-  const T* wp[NA];
-  if constexpr (EPI == EPI_SWIGLU) {
-    wp[0] = reinterpret_cast<const T*>(a.w[0]) + (size_t)f_safe * K;
-    wp[1] = reinterpret_cast<const T*>(a.w[1]) + (size_t)f_safe * K;
-  } else {
-    wp[0] = seg_row<T>(a, f_safe);
-  }
-  // Token rows of this lane.
-  const T* xp[CT];
-  bool tv[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int m = ct * 16 + r16;
-    tv[ct] = m < a.M;
-    xp[ct] = reinterpret_cast<const T*>(a.x) + (size_t)(tv[ct] ? m : 0) * K;
-  }
-  const T* gp = reinterpret_cast<const T*>(a.gamma);
-
-  const int nkb = (K + KB - 1) / KB;
-  const int kb0 = (nkb * wave) / NW;
-  const int kb1 = (nkb * (wave + 1)) / NW;
-
-  f32x4 acc[NA][CT];
-#pragma unroll
-  for (int n = 0; n < NA; ++n)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[n][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ssq[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) ssq[ct] = 0.f;
-
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 wa[2][NA][4];
-  // Software pipeline: weights of block kb+1 are in flight while kb is consumed.
-  auto load_w = [&](int buf, int kb) {
-    const int kbase = kb * KB + kg * 4 * E;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int k = kbase + s * E;
-#pragma unroll
-      for (int n = 0; n < NA; ++n) wa[buf][n][s] = (k < K) ? ld16(wp[n] + k) : zero;
-    }
-  };
-  if (kb0 < kb1) load_w(0, kb0);
-  int buf = 0;
-  for (int kb = kb0; kb < kb1; ++kb) {
-    if (kb + 1 < kb1) load_w(buf ^ 1, kb + 1);
-    const int kbase = kb * KB + kg * 4 * E;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int k = kbase + s * E;
-      const bool inb = k < K;
-      u32x4 gv = zero;
-      if constexpr (NORM) gv = inb ? ld16(gp + k) : zero;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        u32x4 xv = (inb && tv[ct]) ? ld16(xp[ct] + k) : zero;
-        if constexpr (NORM) {
-          float xf[E], gf[E];
-          unpack16<DT>(xv, xf);
-          unpack16<DT>(gv, gf);
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            ssq[ct] += xf[e] * xf[e];
-            xf[e] *= gf[e];
-          }
-          xv = pack16<DT>(xf);
-        }
-#pragma unroll
-        for (int n = 0; n < NA; ++n) acc[n][ct] = mfma16_chunk<DT>(wa[buf][n][s], xv, acc[n][ct]);
-      }
-    }
-    buf ^= 1;
-  }
-
-  // Cross-wave reduction.
   __shared__ f32x4 red[NW > 1 ? NW - 1 : 1][NA * CT][64];
-  __shared__ float ssq_s[NW][CT * 16];
-  if constexpr (NORM) {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      float v = ssq[ct];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (kg == 0) ssq_s[wave][ct * 16 + r16] = v;
-    }
-  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
   if (wave > 0) {
 #pragma unroll
     for (int n = 0; n < NA; ++n)
@@ -137,19 +56,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(ProjArgs a) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[n][ct] += red[w - 1][n * CT + ct][lane];
 
-  // Epilogue: lane holds token column r16 (+16 ct), features row0 + kg*4 + 0..3.
+  // Lane holds token r16 (+16 ct), features row0 + kg*4 + 0..3.
   const int f = row0 + kg * 4;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int m = ct * 16 + r16;
     if (m >= a.M) continue;
-    float scale = 1.f;
-    if constexpr (NORM) {
-      float tot = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) tot += ssq_s[w][ct * 16 + r16];
-      scale = 1.0f / sqrtf(tot / (float)K + a.eps);
-    }
+    const float scale = scale_tok ? scale_tok[m] : 1.f;
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = acc[0][ct][i] * scale;
@@ -169,7 +82,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(ProjArgs a) {
       } else if constexpr (EPI == EPI_SWIGLU) {
         float o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = silu(v[i]) * (acc[1][ct][i] * scale);
+        for (int i = 0; i < 4; ++i) o[i] = silu(v[i]) * (acc[NA - 1][ct][i] * scale);
         T* y = reinterpret_cast<T*>(a.y) + (size_t)m * a.N + f;
         store4<DT>(y, o[0], o[1], o[2], o[3]);
       } else {  // EPI_QKV
@@ -179,27 +92,442 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(ProjArgs a) {
   }
 }
 
-template <int DT, int EPI, bool NORM>
-static hipError_t gemv_dispatch(const ProjArgs& a, hipStream_t s) {
-  const int grid = (a.N + 15) / 16;
-  const bool wide = grid <= 512;  // few row tiles: split K over 8 waves instead of 4
-  if (a.M <= 16) {
-    if (wide) hipLaunchKernelGGL((gemv_kernel<DT, EPI, NORM, 1, 8>), dim3(grid), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemv_kernel<DT, EPI, NORM, 1, 4>), dim3(grid), dim3(256), 0, s, a);
+// Weight row pointers of this lane (rows past N read row 0; dropped later).
+template <int DT, int EPI, int NA>
+__device__ __forceinline__ void gemv_rows(const ProjArgs& a, int row0,
+                                          const typename Elt<DT>::T* (&wp)[NA]) {
+  typedef typename Elt<DT>::T T;
+  const int f_lane = row0 + (threadIdx.x & 15);
+  const int f_safe = f_lane < a.N ? f_lane : 0;
+  if constexpr (EPI == EPI_SWIGLU) {
+    wp[0] = reinterpret_cast<const T*>(a.w[0]) + (size_t)f_safe * a.K;
+    wp[NA - 1] = reinterpret_cast<const T*>(a.w[1]) + (size_t)f_safe * a.K;
   } else {
-    if (wide) hipLaunchKernelGGL((gemv_kernel<DT, EPI, NORM, 2, 8>), dim3(grid), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemv_kernel<DT, EPI, NORM, 2, 4>), dim3(grid), dim3(256), 0, s, a);
+    wp[0] = seg_row<T>(a, f_safe);
   }
+}
+
+template <int DT, int EPI, bool NORM, int NW, int PF>
+__global__ __launch_bounds__(NW * 64) void gemv_lds_kernel(ProjArgs a) {
+  typedef typename Elt<DT>::T T;
+  constexpr int E = Elt<DT>::PER16;   // elements per 16-byte chunk
+  constexpr int KB = 16 * E;          // k per block: 4 lane groups x 4 chunks
+  constexpr int NA = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int NS = PF + 1;          // ring slots
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  T* xs = reinterpret_cast<T*>(smem);  // [M][K]
+  __shared__ float rstd_s[16];
+  __shared__ float part_s[NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int K = a.K, M = a.M;
+  const int row0 = blockIdx.x * 16;
+
+  const T* wp[NA];
+  gemv_rows<DT, EPI, NA>(a, row0, wp);
+  const int nkb = (K + KB - 1) / KB;
+  const int kb0 = (nkb * wave) / NW;
+  const int kb1 = (nkb * (wave + 1)) / NW;
+
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 wa[NS][NA][4];
+  auto load_w = [&](auto slot, int kb) {
+    constexpr int S = decltype(slot)::value;
+    const int kbase = kb * KB + kg * 4 * E;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = kbase + s * E;
+#pragma unroll
+      for (int n = 0; n < NA; ++n) wa[S][n][s] = (k < K) ? ld16(wp[n] + k) : zero;
+    }
+  };
+  // Start the weight stream before staging the activations.
+  if (kb0 < kb1) load_w(ic<0>{}, kb0);
+  if constexpr (PF >= 2) {
+    if (kb0 + 1 < kb1) load_w(ic<1>{}, kb0 + 1);
+  }
+
+  // Stage activations (times the gain when the norm is fused).
+  const int KC = K / E;
+  const T* xg = reinterpret_cast<const T*>(a.x);
+  const T* gg = reinterpret_cast<const T*>(a.gamma);
+  for (int m = 0; m < M; ++m) {
+    float ss = 0.f;
+    for (int c = tid; c < KC; c += NW * 64) {
+      u32x4 xv = ld16(xg + (size_t)m * K + c * E);
+      if constexpr (NORM) {
+        float xf[E], gf[E];
+        unpack16<DT>(xv, xf);
+        unpack16<DT>(ld16(gg + c * E), gf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          ss += xf[e] * xf[e];
+          xf[e] *= gf[e];
+        }
+        xv = pack16<DT>(xf);
+      }
+      st16(xs + (size_t)m * K + c * E, xv);
+    }
+    if constexpr (NORM) {
+      ss = wave_sum(ss);
+      if (lane == 0) part_s[wave] = ss;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += part_s[w];
+        rstd_s[m] = 1.0f / sqrtf(t / (float)K + a.eps);
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[NA][1];
+#pragma unroll
+  for (int n = 0; n < NA; ++n) acc[n][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool tv = r16 < M;
+  const T* xl = xs + (size_t)(tv ? r16 : 0) * K;
+
+  auto step = [&](auto slot, int kb) {
+    constexpr int S = decltype(slot)::value;
+    if (kb + PF < kb1) load_w(ic<(S + PF) % NS>{}, kb + PF);
+    const int kbase = kb * KB + kg * 4 * E;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = kbase + s * E;
+      const u32x4 xv = (tv && k < K) ? ld16(xl + k) : zero;
+#pragma unroll
+      for (int n = 0; n < NA; ++n) acc[n][0] = mfma16_chunk<DT>(wa[S][n][s], xv, acc[n][0]);
+    }
+  };
+  for (int kb = kb0; kb < kb1; kb += NS) {
+    step(ic<0>{}, kb);
+    if (kb + 1 < kb1) step(ic<1 % NS>{}, kb + 1);
+    if constexpr (NS > 2) {
+      if (kb + 2 < kb1) step(ic<2 % NS>{}, kb + 2);
+    }
+  }
+  gemv_finish<DT, EPI, NA, 1, NW>(a, acc, NORM ? rstd_s : nullptr, row0);
+}
+
+template <int DT, int EPI, int CT, int NW, int PF>
+__global__ __launch_bounds__(NW * 64) void gemv_glb_kernel(ProjArgs a) {
+  typedef typename Elt<DT>::T T;
+  constexpr int E = Elt<DT>::PER16;
+  constexpr int KB = 16 * E;
+  constexpr int NA = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int NS = PF + 1;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int K = a.K;
+  const int row0 = blockIdx.x * 16;
+  const T* wp[NA];
+  gemv_rows<DT, EPI, NA>(a, row0, wp);
+  const T* xp[CT];
+  bool tv[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int m = ct * 16 + r16;
+    tv[ct] = m < a.M;
+    xp[ct] = reinterpret_cast<const T*>(a.x) + (size_t)(tv[ct] ? m : 0) * K;
+  }
+  const int nkb = (K + KB - 1) / KB;
+  const int kb0 = (nkb * wave) / NW;
+  const int kb1 = (nkb * (wave + 1)) / NW;
+
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 wa[NS][NA][4];
+  u32x4 xa[NS][CT][4];
+  auto load_w = [&](auto slot, int kb) {
+    constexpr int S = decltype(slot)::value;
+    const int kbase = kb * KB + kg * 4 * E;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = kbase + s * E;
+#pragma unroll
+      for (int n = 0; n < NA; ++n) wa[S][n][s] = (k < K) ? ld16(wp[n] + k) : zero;
+    }
+  };
+  auto load_x = [&](auto slot, int kb) {
+    constexpr int S = decltype(slot)::value;
+    const int kbase = kb * KB + kg * 4 * E;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = kbase + s * E;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) xa[S][ct][s] = (k < K && tv[ct]) ? ld16(xp[ct] + k) : zero;
+    }
+  };
+  if (kb0 < kb1) {
+    load_x(ic<0>{}, kb0);
+    load_w(ic<0>{}, kb0);
+  }
+  if constexpr (PF >= 2) {
+    if (kb0 + 1 < kb1) load_w(ic<1>{}, kb0 + 1);
+  }
+  f32x4 acc[NA][CT];
+#pragma unroll
+  for (int n = 0; n < NA; ++n)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[n][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Per step: activations of the next block, then weights PF blocks ahead
+  // (issue order keeps the in-order load counter from waiting on the ring).
+  auto step = [&](auto slot, int kb) {
+    constexpr int S = decltype(slot)::value;
+    if (kb + 1 < kb1) load_x(ic<(S + 1) % NS>{}, kb + 1);
+    if (kb + PF < kb1) load_w(ic<(S + PF) % NS>{}, kb + PF);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int n = 0; n < NA; ++n)
+          acc[n][ct] = mfma16_chunk<DT>(wa[S][n][s], xa[S][ct][s], acc[n][ct]);
+  };
+  for (int kb = kb0; kb < kb1; kb += NS) {
+    step(ic<0>{}, kb);
+    if (kb + 1 < kb1) step(ic<1 % NS>{}, kb + 1);
+    if constexpr (NS > 2) {
+      if (kb + 2 < kb1) step(ic<2 % NS>{}, kb + 2);
+    }
+  }
+  gemv_finish<DT, EPI, NA, CT, NW>(a, acc, nullptr, blockIdx.x * 16);
+}
+
+// ---------------------------------------------------------------------------
+// One to four tokens: each wave owns R output rows (R gate + R up rows for
+// SwiGLU) over the full K.  Lane l reads the 16-byte chunks l, l+64, ... of a
+// row, so every load instruction covers 1 KB of one row contiguously; the
+// activations (times the gain for a fused norm) are staged once per
+// workgroup in LDS and read back as 16-byte chunks; float32 dot products are
+// summed across the wave at the end.  With R rows per wave there are N/R waves
+// in flight, enough to balance any projection over the 256 CUs.
+// ---------------------------------------------------------------------------
+template <int DT, int EPI, bool NORM, int MT, int R>
+__global__ __launch_bounds__(256) void gemv_row_kernel(ProjArgs a) {
+  typedef typename Elt<DT>::T T;
+  constexpr int E = Elt<DT>::PER16;
+  constexpr int NA = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int U = (R * NA >= 4) ? 4 : 8;  // chunks per row loaded per batch
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  T* xs = reinterpret_cast<T*>(smem);  // [M][K]
+  __shared__ float rstd_s[MT];
+  __shared__ float part_s[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, M = a.M;
+  const int f0 = (blockIdx.x * 4 + wave) * R;  // first row of this wave
+
+  // Row pointers (rows past N read row 0; results dropped).
+  const T* wp[NA][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int f = f0 + r < a.N ? f0 + r : 0;
+    if constexpr (EPI == EPI_SWIGLU) {
+      wp[0][r] = reinterpret_cast<const T*>(a.w[0]) + (size_t)f * K;
+      wp[1][r] = reinterpret_cast<const T*>(a.w[1]) + (size_t)f * K;
+    } else {
+      wp[0][r] = seg_row<T>(a, f);
+    }
+  }
+  const int nch = (K + 64 * E - 1) / (64 * E);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 wv[U][NA][R];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (c0 + u) * 64 * E + lane * E;
+#pragma unroll
+      for (int n = 0; n < NA; ++n)
+#pragma unroll
+        for (int r = 0; r < R; ++r) wv[u][n][r] = (k < K) ? ld16(wp[n][r] + k) : zero;
+    }
+  };
+  // Weight loads start before the activations are staged.
+  load_batch(0);
+
+  const int KC = K / E;
+  const T* xg = reinterpret_cast<const T*>(a.x);
+  const T* gg = reinterpret_cast<const T*>(a.gamma);
+  for (int m = 0; m < M; ++m) {
+    float ss = 0.f;
+    for (int c = tid; c < KC; c += 256) {
+      u32x4 xv = ld16(xg + (size_t)m * K + c * E);
+      if constexpr (NORM) {
+        float xf[E], gf[E];
+        unpack16<DT>(xv, xf);
+        unpack16<DT>(ld16(gg + c * E), gf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          ss += xf[e] * xf[e];
+          xf[e] *= gf[e];
+        }
+        xv = pack16<DT>(xf);
+      }
+      st16(xs + (size_t)m * K + c * E, xv);
+    }
+    if constexpr (NORM) {
+      ss = wave_sum(ss);
+      if (lane == 0) part_s[wave] = ss;
+      __syncthreads();
+      if (tid == 0)
+        rstd_s[m] = 1.0f / sqrtf((part_s[0] + part_s[1] + part_s[2] + part_s[3]) / (float)K + a.eps);
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  float acc[NA][R][MT];
+#pragma unroll
+  for (int n = 0; n < NA; ++n)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[n][r][m] = 0.f;
+
+  for (int c0 = 0; c0 < nch; c0 += U) {
+    if (c0 > 0) load_batch(c0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (c0 + u) * 64 * E + lane * E;
+      if (k >= K) break;
+      float wf[NA][R][E];
+#pragma unroll
+      for (int n = 0; n < NA; ++n)
+#pragma unroll
+        for (int r = 0; r < R; ++r) unpack16<DT>(wv[u][n][r], wf[n][r]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+          float xf[E];
+          unpack16<DT>(ld16(xs + (size_t)m * K + k), xf);
+#pragma unroll
+          for (int n = 0; n < NA; ++n)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int e = 0; e < E; ++e) acc[n][r][m] += wf[n][r][e] * xf[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NA; ++n)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[n][r][m] = wave_sum(acc[n][r][m]);
+  if (lane != 0) return;
+
+  for (int m = 0; m < M && m < MT; ++m) {
+    const float scale = NORM ? rstd_s[m] : 1.f;
+    if constexpr (EPI == EPI_QKV) {
+      // R is even and f0 is even: rows come in RoPE pairs of 4 (two pairs)
+#pragma unroll
+      for (int r = 0; r < R; r += 4) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = acc[0][r + i][m] * scale;
+        if (f0 + r < a.N) qkv_epilogue4<DT>(a, a.tok0 + m, m, f0 + r, v);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int f = f0 + r;
+        if (f >= a.N) break;
+        const float v = acc[0][r][m] * scale;
+        if constexpr (EPI == EPI_LOGITS) {
+          reinterpret_cast<float*>(a.y)[(size_t)m * a.N + f] = v;
+        } else if constexpr (EPI == EPI_RESID) {
+          const T* rp = reinterpret_cast<const T*>(a.resid) + (size_t)m * a.N + f;
+          reinterpret_cast<T*>(a.y)[(size_t)m * a.N + f] = Elt<DT>::from_f32(Elt<DT>::to_f32(*rp) + v);
+        } else {  // SwiGLU
+          const float up = acc[NA - 1][r][m] * scale;
+          reinterpret_cast<T*>(a.y)[(size_t)m * a.N + f] = Elt<DT>::from_f32(silu(v) * up);
+        }
+      }
+    }
+  }
+}
+
+size_t gemv_lds_bytes(int dt, int M, int K) { return (size_t)M * K * (dt == DT_F32 ? 4 : 2); }
+
+bool gemv_fits_lds(int dt, int M, int K) {
+  return M <= 16 && gemv_lds_bytes(dt, M, K) <= (size_t)GEMV_LDS_BYTES;
+}
+
+template <int DT, int EPI, bool NORM>
+static hipError_t gemv_lds_launch(const ProjArgs& a, hipStream_t s) {
+  const int grid = (a.N + 15) / 16;
+  const size_t sh = gemv_lds_bytes(DT, a.M, a.K);
+  if (grid <= 1024)  // few row tiles: split K over 8 waves
+    hipLaunchKernelGGL((gemv_lds_kernel<DT, EPI, NORM, 8, 2>), dim3(grid), dim3(512), sh, s, a);
+  else
+    hipLaunchKernelGGL((gemv_lds_kernel<DT, EPI, NORM, 4, 2>), dim3(grid), dim3(256), sh, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int EPI>
+static hipError_t gemv_glb_launch(const ProjArgs& a, hipStream_t s) {
+  const int grid = (a.N + 15) / 16;
+  if (a.M <= 16)
+    hipLaunchKernelGGL((gemv_glb_kernel<DT, EPI, 1, 4, 2>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemv_glb_kernel<DT, EPI, 2, 4, 1>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int EPI, bool NORM>
+static hipError_t gemv_row_launch(const ProjArgs& a, hipStream_t s) {
+  constexpr int R = (EPI == EPI_QKV) ? 4 : 2;  // QKV: two RoPE pairs per wave
+  const int grid = (a.N + 4 * R - 1) / (4 * R);
+  const size_t sh = gemv_lds_bytes(DT, a.M, a.K);
+  if (a.M == 1)
+    hipLaunchKernelGGL((gemv_row_kernel<DT, EPI, NORM, 1, R>), dim3(grid), dim3(256), sh, s, a);
+  else
+    hipLaunchKernelGGL((gemv_row_kernel<DT, EPI, NORM, 4, R>), dim3(grid), dim3(256), sh, s, a);
   return hipGetLastError();
 }
 
 template <int DT>
 static hipError_t gemv_dt(int epi, const ProjArgs& a, hipStream_t s) {
+  const bool norm = a.gamma != nullptr;
+  if (a.M <= 4 && gemv_fits_lds(DT, a.M, a.K)) {
+    switch (epi) {
+      case EPI_QKV: return norm ? gemv_row_launch<DT, EPI_QKV, true>(a, s)
+                                : gemv_row_launch<DT, EPI_QKV, false>(a, s);
+      case EPI_RESID: return gemv_row_launch<DT, EPI_RESID, false>(a, s);
+      case EPI_SWIGLU: return norm ? gemv_row_launch<DT, EPI_SWIGLU, true>(a, s)
+                                   : gemv_row_launch<DT, EPI_SWIGLU, false>(a, s);
+      case EPI_LOGITS: return norm ? gemv_row_launch<DT, EPI_LOGITS, true>(a, s)
+                                   : gemv_row_launch<DT, EPI_LOGITS, false>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (gemv_fits_lds(DT, a.M, a.K)) {
+    switch (epi) {
+      case EPI_QKV: return norm ? gemv_lds_launch<DT, EPI_QKV, true>(a, s)
+                                : gemv_lds_launch<DT, EPI_QKV, false>(a, s);
+      case EPI_RESID: return gemv_lds_launch<DT, EPI_RESID, false>(a, s);
+      case EPI_SWIGLU: return norm ? gemv_lds_launch<DT, EPI_SWIGLU, true>(a, s)
+                                   : gemv_lds_launch<DT, EPI_SWIGLU, false>(a, s);
+      case EPI_LOGITS: return norm ? gemv_lds_launch<DT, EPI_LOGITS, true>(a, s)
+                                   : gemv_lds_launch<DT, EPI_LOGITS, false>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (norm) return hipErrorInvalidValue;  // the caller normalises first
   switch (epi) {
-    case EPI_QKV: return gemv_dispatch<DT, EPI_QKV, true>(a, s);
-    case EPI_RESID: return gemv_dispatch<DT, EPI_RESID, false>(a, s);
-    case EPI_SWIGLU: return gemv_dispatch<DT, EPI_SWIGLU, true>(a, s);
-    case EPI_LOGITS: return gemv_dispatch<DT, EPI_LOGITS, true>(a, s);
+    case EPI_QKV: return gemv_glb_launch<DT, EPI_QKV>(a, s);
+    case EPI_RESID: return gemv_glb_launch<DT, EPI_RESID>(a, s);
+    case EPI_SWIGLU: return gemv_glb_launch<DT, EPI_SWIGLU>(a, s);
+    case EPI_LOGITS: return gemv_glb_launch<DT, EPI_LOGITS>(a, s);
   }
   return hipErrorInvalidValue;
 }

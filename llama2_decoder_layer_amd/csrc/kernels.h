@@ -37,7 +37,10 @@ struct ProjArgs {
   const float* rsin;
 };
 
+// Decode-sized projection (M <= 32 tokens).  A fused norm (gamma != nullptr)
+// needs the M activation rows to fit the LDS stage: gemv_fits_lds(dt, M, K).
 hipError_t launch_gemv(int dt, int epi, const ProjArgs& a, hipStream_t s);
+bool gemv_fits_lds(int dt, int M, int K);
 hipError_t launch_gemm(int dt, int epi, const ProjArgs& a, hipStream_t s);
 
 // RMSNorm of `rows` rows of width H: u = x / sqrt(mean(x^2) + eps) * gamma.
@@ -61,6 +64,14 @@ struct AttnDecodeArgs {
   void* o;               // [nq, nh*hd] act dtype
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
+// Query heads served per workgroup for a GQA group of g heads.
+int attn_heads_per_group(int g);
+// Keys per split for the launch (one of 2, 4 or 8 x 256/(hd/8)), or -1 when
+// the context needs more than ATTN_MAX_SPLITS splits of the largest chunk.
+constexpr int ATTN_MAX_SPLITS = 1024;
+int attn_pick_chunk(int hd, int max_keys, int queries, int nkv, int g);
+// Smallest chunk attn_pick_chunk returns (sizes the workspace).
+inline int attn_min_chunk(int hd) { return 2 * (256 / (hd / 8)); }
 
 // Causal prefill attention with MFMA (16-bit formats).
 struct AttnPrefillArgs {

@@ -5,7 +5,7 @@
 // workspace size is known in advance):
 //  * "token-skinny" (decode, and prefill of <= 32 tokens or float32):
 //      QKV projection with fused RMSNorm + RoPE + cache append  (gemv)
-//      split-over-context attention + log-sum-exp combine        (attn_decode)
+//      split-over-context attention + log-sum-exp merge          (attn_decode)
 //      O projection + residual                                   (gemv)
 //      gate/up projection with fused RMSNorm + SwiGLU            (gemv)
 //      down projection + residual                                (gemv)
@@ -107,8 +107,6 @@ static bool wide_plan(const ll_config* c, int64_t tokens_total, bool decode) {
   return !decode && c->act_dtype != LL_F32 && tokens_total > 32;
 }
 
-constexpr int CHUNK_MIN = 64;
-
 struct Layout {
   size_t q32, pm, pl, pacc, u, q16, o, h1, a, total;
   int nsplit_max;
@@ -126,7 +124,9 @@ static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide) {
   } else {
     // Token-skinny plans process at most 32 tokens at a time.
     const int64_t g = std::min<int64_t>(bt, 32);
-    L.nsplit_max = (s_max + CHUNK_MIN - 1) / CHUNK_MIN;
+    const int cmin = attn_min_chunk(c->head_dim);
+    L.nsplit_max = (s_max + cmin - 1) / cmin;
+    L.u = take(g * c->hidden * act);   // norm pre-pass when the LDS stage is too small
     L.q32 = take(g * qd * 4);
     L.pm = take(g * c->n_heads * L.nsplit_max * 4);
     L.pl = take(g * c->n_heads * L.nsplit_max * 4);
@@ -137,17 +137,6 @@ static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide) {
   L.a = take(bt * c->intermediate * act);
   L.total = off;
   return L;
-}
-
-static int pick_chunk(int max_keys, int queries, int heads_groups) {
-  // Largest power-of-two chunk in [64, 512] that still gives >= 2048 workgroups.
-  int chunk = 512;
-  while (chunk > CHUNK_MIN) {
-    const int64_t wgs = (int64_t)((max_keys + chunk - 1) / chunk) * queries * heads_groups;
-    if (wgs >= 2048) break;
-    chunk >>= 1;
-  }
-  return chunk;
 }
 
 // ---------------------------------------------------------------------------
@@ -184,12 +173,24 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
   uint8_t* h1 = ws + L.h1 + tok0 * H * act;
   uint8_t* a = ws + L.a + tok0 * I * act;
 
+  // RMSNorm is fused into the projection when the m activation rows fit its
+  // LDS stage; otherwise a norm pass writes u first.
+  const bool fuse_norm = gemv_fits_lds(dt, m, H);
+  void* u = ws + L.u;
+
   // 1. QKV + RMSNorm + RoPE + cache append.
   ProjArgs p = base_args(c);
   p.w[0] = w->w_q; p.w[1] = w->w_k; p.w[2] = w->w_v;
   p.seg1 = qd; p.seg2 = qd + kd;
   p.N = qd + 2 * kd; p.K = H; p.M = m; p.tok0 = (int)tok0;
-  p.x = xm; p.gamma = w->attn_norm;
+  if (fuse_norm) {
+    p.x = xm; p.gamma = w->attn_norm;
+  } else {
+    timer_before(KID_RMSNORM, s);
+    LL_TRY(launch_rmsnorm(dt, xm, w->attn_norm, u, m, H, c->eps, s));
+    timer_after(KID_RMSNORM, s);
+    p.x = u;
+  }
   p.q32 = (float*)(ws + L.q32);
   p.kc = kc; p.vc = vc; p.ctx_len = ctx_len; p.start_pos = start_pos; p.T = T;
   p.max_ctx = max_ctx; p.s_max = s_max; p.rcos = w->rope_cos; p.rsin = w->rope_sin;
@@ -204,9 +205,8 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
   at.T = T; at.max_ctx = max_ctx; at.nq = m; at.nh = c->n_heads; at.nkv = c->n_kv_heads;
   at.hd = c->head_dim; at.s_max = s_max; at.kv_dt = c->kv_dtype; at.act_dt = dt;
   const int max_keys = ctx_len ? max_ctx + 1 : start_pos + T;
-  const int g = c->n_heads / c->n_kv_heads;
-  const int gc = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
-  at.chunk = pick_chunk(max_keys, m, c->n_kv_heads * (g / gc));
+  at.chunk = attn_pick_chunk(c->head_dim, max_keys, m, c->n_kv_heads, c->n_heads / c->n_kv_heads);
+  if (at.chunk < 0) return LL_EUNSUPPORTED;
   at.nsplit = (max_keys + at.chunk - 1) / at.chunk;
   if (at.nsplit > L.nsplit_max) return LL_EWORKSPACE;
   at.part_m = (float*)(ws + L.pm); at.part_l = (float*)(ws + L.pl);
@@ -243,7 +243,15 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
   // 4. gate/up + RMSNorm + SwiGLU.
   ProjArgs pg = base_args(c);
   pg.w[0] = w->w_gate; pg.w[1] = w->w_up;
-  pg.N = I; pg.K = H; pg.M = m; pg.x = h1; pg.gamma = w->ffn_norm; pg.y = a;
+  pg.N = I; pg.K = H; pg.M = m; pg.y = a;
+  if (fuse_norm) {
+    pg.x = h1; pg.gamma = w->ffn_norm;
+  } else {
+    timer_before(KID_RMSNORM, s);
+    LL_TRY(launch_rmsnorm(dt, h1, w->ffn_norm, u, m, H, c->eps, s));
+    timer_after(KID_RMSNORM, s);
+    pg.x = u;
+  }
   timer_before(KID_GEMV_GATEUP, s);
   LL_TRY(launch_gemv(dt, EPI_SWIGLU, pg, s));
   timer_after(KID_GEMV_GATEUP, s);
@@ -429,11 +437,15 @@ int llama_head_argmax(const void* final_norm, const void* w_lm, const void* h, i
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   const size_t esz = esize(dtype);
-  for (int r0 = 0; r0 < n; r0 += 32) {
+  // Rows go through the fused-norm projection in groups whose activations fit its LDS stage.
+  int group = 16;
+  while (group > 1 && !gemv_fits_lds(dtype, group, hidden)) group >>= 1;
+  if (!gemv_fits_lds(dtype, group, hidden)) return LL_EUNSUPPORTED;
+  for (int r0 = 0; r0 < n; r0 += group) {
     ProjArgs p;
     memset(&p, 0, sizeof(p));
     p.w[0] = w_lm; p.seg1 = p.seg2 = vocab;
-    p.N = vocab; p.K = hidden; p.M = std::min(32, n - r0);
+    p.N = vocab; p.K = hidden; p.M = std::min(group, n - r0);
     p.x = (const uint8_t*)h + (size_t)r0 * hidden * esz;
     p.gamma = final_norm; p.eps = eps;
     p.y = logits + (size_t)r0 * vocab;
