@@ -177,7 +177,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnDecodeArgs a) {
     a.part_m[pi] = s_m[tid];
     a.part_l[pi] = s_l[tid];
   }
-
 }
 
 // Merge of the splits of one (query, head group).  The 256 threads form
