@@ -8,7 +8,8 @@
 // the probabilities it holds are already the B operand of O^T = V^T P^T -- the
 // MFMA k order is chosen to match the keys each lane holds.  K is staged in LDS
 // row-major (16-byte chunks XOR-swizzled); V is staged transposed, [d][key], so
-// the A operand of the second product is two 8-byte LDS reads.  Tiles entirely
+// the A operand of the second product is two 8-byte LDS reads (its padded row
+// of 68 elements puts the 32 rows of one read on distinct banks).  Tiles entirely
 // above a wave's last query are skipped; only diagonal tiles are masked.  The
 // latest (most expensive) query blocks are launched first.
 #include "common.cuh"
@@ -25,6 +26,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   typedef typename Elt<DT>::T ET;
   constexpr int CPR = HD / 8;          // 16-byte chunks per key row
   constexpr int KPT = HD / 32;         // keys per thread in the V transpose
+  // K rows are HD*2 bytes; XOR the 16-byte chunk index with bits of the row so
+  // the 16 rows of one ds_read_b128 cycle hit distinct bank groups (256-byte
+  // rows: the low four bits; 128-byte rows, two per bank sweep: bits 1..3).
+  auto ksw = [](int kr) { return HD == 128 ? (kr & 15) : ((kr >> 1) & 7); };
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[PKV * HD];
   __shared__ __attribute__((aligned(16))) uint16_t lds_vt[HD * VT_STRIDE];
 
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
       const int kr = idx / CPR, c = idx - kr * CPR;
       const int key = key0 + kr;
       const u32x4 v = (key < kv_end) ? ld16(kbase + (size_t)key * HD + c * 8) : zero;
-      st16(&lds_k[kr * HD + ((c ^ (kr & 7)) << 3)], v);
+      st16(&lds_k[kr * HD + ((c ^ ksw(kr)) << 3)], v);
     }
     // V tile -> LDS transposed: thread takes KPT keys x 8 dims.
     {
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int kr = kb * 32 + l32;
-        const u32x4 kf = ld16(&lds_k[kr * HD + ((ch ^ (kr & 7)) << 3)]);
+        const u32x4 kf = ld16(&lds_k[kr * HD + ((ch ^ ksw(kr)) << 3)]);
         sacc[kb] = mfma32<DT>(kf, qf[s], sacc[kb]);
       }
     }

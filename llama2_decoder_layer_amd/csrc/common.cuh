@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ll {
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -17,6 +19,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
+
+// Compile-time index (register-ring slots and unrolled loop parities).
+template <int I>
+using ic = std::integral_constant<int, I>;
 
 // ---------------------------------------------------------------------------
 // Scalar conversions.  float -> bf16/f16 round to nearest even.

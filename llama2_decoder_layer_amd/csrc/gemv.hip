@@ -21,17 +21,12 @@
 //    host normalises first.
 // Epilogues: RoPE + KV-cache append (QKV), residual add (O, down), SwiGLU
 // (gate/up, two weight matrices) or float32 logits (LM head).
-#include <type_traits>
-
 #include "common.cuh"
 #include "epilogue.cuh"
 
 namespace ll {
 
 constexpr int GEMV_LDS_BYTES = 48 * 1024;  // + static LDS stays within 64 KB
-
-template <int I>
-using ic = std::integral_constant<int, I>;
 
 // Cross-wave reduction of the accumulators and the epilogue (wave 0).
 template <int DT, int EPI, int NA, int CT, int NW>
