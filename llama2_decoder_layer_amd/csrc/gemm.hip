@@ -22,6 +22,9 @@ namespace ll {
 
 constexpr int GBK = 64;   // k per stage
 constexpr int GROUP_M = 4;
+#ifndef GEMM_BIG_WAVES
+#define GEMM_BIG_WAVES 8
+#endif
 
 // QKV epilogue of the prefill GEMMs for four consecutive features f..f+3 of
 // token (b, t) at position pos: RoPE on q/k pairs, q to [B, nh, T, hd], k/v
@@ -269,27 +272,32 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-// One wave per SIMD is the design point of the 256 x 256 tile (256 accumulator
-// registers); telling the compiler so lets it keep fragments in flight
-// instead of trading them for an occupancy it cannot reach.
-template <int BM>
-struct DmaOcc { static constexpr int waves = BM == 256 ? 1 : 2; };
+// Occupancy target per SIMD: 4 waves on a 256 x 256 tile hold 256 accumulator
+// registers each (one wave per SIMD); 8 waves hold 128 (two per SIMD, so one
+// wave's barrier and LDS waits overlap the other's MFMAs).  Telling the
+// compiler lets it keep fragments in flight instead of chasing occupancy.
+template <int BM, int NW>
+struct DmaOcc { static constexpr int waves = (BM == 256 && NW == 4) ? 1 : 2; };
 
-template <int DT, int EPI, int BM, int BN, int KVDT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DmaOcc<BM>::waves, DmaOcc<BM>::waves)))
+template <int DT, int EPI, int BM, int BN, int KVDT, int NW>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(DmaOcc<BM, NW>::waves, DmaOcc<BM, NW>::waves)))
 void gemm_dma_kernel(ProjArgs a) {
   typedef typename Elt<DT>::T T;
   constexpr int BK = 32;
   constexpr int NST = 4;
   constexpr int ROWB = BK * 2;                 // 64 bytes per row slice
   constexpr int RPI = 16;                      // rows per 1 KB wave instruction
-  constexpr int AI = BM / RPI / 4;             // A instructions per wave per stage
-  constexpr int BI = BN / RPI / 4;
+  constexpr int AI = BM / RPI / NW;            // A instructions per wave per stage
+  constexpr int BI = BN / RPI / NW;
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int FM = SWI ? BM / 2 : BM;
+  // Wave grid over (rows, tokens): 2 x NW/2; SwiGLU 1 x NW (gate and up rows
+  // of a feature in the same wave).
+  constexpr int WN = SWI ? NW : NW / 2;        // waves along tokens
   constexpr int RB = SWI ? BM / 32 : BM / 64;
-  constexpr int CB = SWI ? BN / 128 : BN / 64;
+  constexpr int CB = BN / WN / 32;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
 
@@ -352,13 +360,13 @@ void gemm_dma_kernel(ProjArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) row_base[r] = r * 32;
 #pragma unroll
-    for (int c = 0; c < CB; ++c) col_base[c] = wave * (BN / 4) + c * 32;
+    for (int c = 0; c < CB; ++c) col_base[c] = wave * (BN / WN) + c * 32;
   } else {
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
     for (int r = 0; r < RB; ++r) row_base[r] = wm * (BM / 2) + r * 32;
 #pragma unroll
-    for (int c = 0; c < CB; ++c) col_base[c] = wn * (BN / 2) + c * 32;
+    for (int c = 0; c < CB; ++c) col_base[c] = wn * (BN / WN) + c * 32;
   }
   const int l32 = lane & 31, h2 = lane >> 5;
   int aoff[RB], boff[CB];  // byte offsets of this lane's fragment rows (chunk added per step)
@@ -499,11 +507,11 @@ static hipError_t gemm_launch(const ProjArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int EPI, int BM, int BN, int KVDT>
+template <int DT, int EPI, int BM, int BN, int KVDT, int NW>
 static hipError_t gemm_dma_launch(const ProjArgs& a, hipStream_t s) {
   const int fm = (EPI == EPI_SWIGLU) ? BM / 2 : BM;
   const int ntiles = ((a.N + fm - 1) / fm) * ((a.M + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<DT, EPI, BM, BN, KVDT>), dim3(ntiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<DT, EPI, BM, BN, KVDT, NW>), dim3(ntiles), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -511,8 +519,8 @@ template <int DT, int EPI, int KVDT>
 static hipError_t gemm_epi(const ProjArgs& a, hipStream_t s) {
   const bool big = use_big_tile(EPI, a.N, a.M);
   if (a.K % 32 == 0)
-    return big ? gemm_dma_launch<DT, EPI, 256, 256, KVDT>(a, s)
-               : gemm_dma_launch<DT, EPI, 128, 128, KVDT>(a, s);
+    return big ? gemm_dma_launch<DT, EPI, 256, 256, KVDT, GEMM_BIG_WAVES>(a, s)
+               : gemm_dma_launch<DT, EPI, 128, 128, KVDT, 4>(a, s);
   return big ? gemm_launch<DT, EPI, 256, 256, KVDT>(a, s) : gemm_launch<DT, EPI, 128, 128, KVDT>(a, s);
 }
 
