@@ -125,6 +125,9 @@ def main():
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run 3 device-to-device copies of MIB MiB (the "
+                         "known-size reference that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -201,11 +204,23 @@ def main():
     el = time.perf_counter() - t0
     kms, kn = B.llama_layer_timer_stop()
     ms_step = el * 1e3 / args.steps
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": act, "data": "synthetic (seeded; see synth.py)"}
     kavg_s = kms / 1e3 / max(kn, 1)
+    # HBM bytes per launch of the dominant kernel from the committed counter
+    # summary (None when absent or taken on other kernel sources).
+    from llama2_decoder_layer_amd.profiling import load_traffic
+    tr = load_traffic(dom, wl.name)
+    traffic = None if tr is None else tr["bytes"]
     if decode:
         by = decode_bytes(s, inp["ctx_len"], act_b, kv_b)
         out.update(value=wl.batch / (ms_step / 1e3), unit="tokens/s/layer")
@@ -214,7 +229,7 @@ def main():
                             "frac_of_peak": layer_gbps / HBM_PEAK_GBPS}
         ach = by[dom] / kavg_s / 1e9
         out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
                            "algorithmic_bytes_per_launch": by[dom], "avg_launch_us": kavg_s * 1e6,
                            "launches_timed": kn}
     else:
@@ -225,7 +240,7 @@ def main():
                              "frac_of_peak": tflops / BF16_PEAK_TFLOPS}
         ach = fl["gate_up"] / kavg_s / 1e12
         out["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                           "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": traffic,
                            "algorithmic_flops_per_launch": fl["gate_up"],
                            "avg_launch_us": kavg_s * 1e6, "launches_timed": kn}
     out["config"] = {"workload": wl.name, "hidden": s.hidden, "n_heads": s.n_heads,

@@ -173,11 +173,15 @@ const char* llama_layer_strerror(int code);
 
 /*
  * Kernel timing (benchmark instrumentation).  llama_layer_timer_start arms
- * HIP-event pairs around up to max_launches future launches of kernel
+ * HIP-event pairs for up to max_launches future launches of kernel
  * `kernel_id` (see llama_layer_kernel_name) on whatever stream they are
- * enqueued; llama_layer_timer_stop waits for those events, writes the summed
- * milliseconds and the number of timed launches, and disarms.  Not thread-safe;
- * creates and destroys HIP events (host-side objects, no device memory).
+ * enqueued.  Each pair is handed to the kernel's dispatch (hipExtLaunchKernel),
+ * which records its own start and end, so a pair measures that kernel's
+ * execution only; where an id covers two kernels (attn_decode: split pass and
+ * merge) the first one is timed.  llama_layer_timer_stop waits for those
+ * events, writes the summed milliseconds and the number of timed launches, and
+ * disarms.  Not thread-safe; creates and destroys HIP events (host-side
+ * objects, no device memory).
  */
 int llama_layer_timer_start(int32_t kernel_id, int32_t max_launches);
 int llama_layer_timer_stop(double* total_ms, int32_t* launches);

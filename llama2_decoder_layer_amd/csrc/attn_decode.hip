@@ -247,9 +247,9 @@ template <int KVDT, int HD, int GC>
 static hipError_t split_launch_kpt(const AttnDecodeArgs& a, dim3 grid, hipStream_t s) {
   constexpr int KPI = 256 / (HD / 8);
   switch (a.chunk / KPI) {
-    case 2: hipLaunchKernelGGL((attn_split_kernel<KVDT, HD, GC, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_split_kernel<KVDT, HD, GC, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_split_kernel<KVDT, HD, GC, 8>), grid, dim3(256), 0, s, a); break;
+    case 2: LL_LAUNCH((attn_split_kernel<KVDT, HD, GC, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: LL_LAUNCH((attn_split_kernel<KVDT, HD, GC, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: LL_LAUNCH((attn_split_kernel<KVDT, HD, GC, 8>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -298,10 +298,10 @@ static hipError_t merge_launch(const AttnDecodeArgs& a, hipStream_t s) {
   dim3 grid(1, a.nkv * (g / gc), a.nq);
   const size_t sh = (size_t)gc * a.nsplit * sizeof(float);
   switch (gc) {
-    case 8: hipLaunchKernelGGL((attn_merge_kernel<HD, 8>), grid, dim3(256), sh, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_merge_kernel<HD, 4>), grid, dim3(256), sh, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_merge_kernel<HD, 2>), grid, dim3(256), sh, s, a); break;
-    default: hipLaunchKernelGGL((attn_merge_kernel<HD, 1>), grid, dim3(256), sh, s, a); break;
+    case 8: LL_LAUNCH((attn_merge_kernel<HD, 8>), grid, dim3(256), sh, s, a); break;
+    case 4: LL_LAUNCH((attn_merge_kernel<HD, 4>), grid, dim3(256), sh, s, a); break;
+    case 2: LL_LAUNCH((attn_merge_kernel<HD, 2>), grid, dim3(256), sh, s, a); break;
+    default: LL_LAUNCH((attn_merge_kernel<HD, 1>), grid, dim3(256), sh, s, a); break;
   }
   return hipGetLastError();
 }

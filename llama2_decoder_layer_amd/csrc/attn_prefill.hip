@@ -208,11 +208,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   dim3 grid((a.T + PQ - 1) / PQ, a.nh, a.B);
   if (a.dt == DT_BF16) {
-    if (a.hd == 128) hipLaunchKernelGGL((attn_prefill_kernel<DT_BF16, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<DT_BF16, 64>), grid, dim3(256), 0, s, a);
+    if (a.hd == 128) LL_LAUNCH((attn_prefill_kernel<DT_BF16, 128>), grid, dim3(256), 0, s, a);
+    else LL_LAUNCH((attn_prefill_kernel<DT_BF16, 64>), grid, dim3(256), 0, s, a);
   } else if (a.dt == DT_F16) {
-    if (a.hd == 128) hipLaunchKernelGGL((attn_prefill_kernel<DT_F16, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<DT_F16, 64>), grid, dim3(256), 0, s, a);
+    if (a.hd == 128) LL_LAUNCH((attn_prefill_kernel<DT_F16, 128>), grid, dim3(256), 0, s, a);
+    else LL_LAUNCH((attn_prefill_kernel<DT_F16, 64>), grid, dim3(256), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

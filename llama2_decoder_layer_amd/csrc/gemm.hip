@@ -503,7 +503,7 @@ template <int DT, int EPI, int BM, int BN, int KVDT>
 static hipError_t gemm_launch(const ProjArgs& a, hipStream_t s) {
   const int fm = (EPI == EPI_SWIGLU) ? BM / 2 : BM;
   const int ntiles = ((a.N + fm - 1) / fm) * ((a.M + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<DT, EPI, BM, BN, KVDT>), dim3(ntiles), dim3(256), 0, s, a);
+  LL_LAUNCH((gemm_kernel<DT, EPI, BM, BN, KVDT>), dim3(ntiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -511,7 +511,7 @@ template <int DT, int EPI, int BM, int BN, int KVDT, int NW>
 static hipError_t gemm_dma_launch(const ProjArgs& a, hipStream_t s) {
   const int fm = (EPI == EPI_SWIGLU) ? BM / 2 : BM;
   const int ntiles = ((a.N + fm - 1) / fm) * ((a.M + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<DT, EPI, BM, BN, KVDT, NW>), dim3(ntiles), dim3(NW * 64), 0, s, a);
+  LL_LAUNCH((gemm_dma_kernel<DT, EPI, BM, BN, KVDT, NW>), dim3(ntiles), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -462,9 +462,9 @@ static hipError_t gemv_lds_launch(const ProjArgs& a, hipStream_t s) {
   const int grid = (a.N + 15) / 16;
   const size_t sh = gemv_lds_bytes(DT, a.M, a.K);
   if (grid <= 1024)  // few row tiles: split K over 8 waves
-    hipLaunchKernelGGL((gemv_lds_kernel<DT, EPI, NORM, 8, 2>), dim3(grid), dim3(512), sh, s, a);
+    LL_LAUNCH((gemv_lds_kernel<DT, EPI, NORM, 8, 2>), dim3(grid), dim3(512), sh, s, a);
   else
-    hipLaunchKernelGGL((gemv_lds_kernel<DT, EPI, NORM, 4, 2>), dim3(grid), dim3(256), sh, s, a);
+    LL_LAUNCH((gemv_lds_kernel<DT, EPI, NORM, 4, 2>), dim3(grid), dim3(256), sh, s, a);
   return hipGetLastError();
 }
 
@@ -472,9 +472,9 @@ template <int DT, int EPI>
 static hipError_t gemv_glb_launch(const ProjArgs& a, hipStream_t s) {
   const int grid = (a.N + 15) / 16;
   if (a.M <= 16)
-    hipLaunchKernelGGL((gemv_glb_kernel<DT, EPI, 1, 4, 2>), dim3(grid), dim3(256), 0, s, a);
+    LL_LAUNCH((gemv_glb_kernel<DT, EPI, 1, 4, 2>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemv_glb_kernel<DT, EPI, 2, 4, 1>), dim3(grid), dim3(256), 0, s, a);
+    LL_LAUNCH((gemv_glb_kernel<DT, EPI, 2, 4, 1>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -484,9 +484,9 @@ static hipError_t gemv_row_launch(const ProjArgs& a, hipStream_t s) {
   const int grid = (a.N + 4 * R - 1) / (4 * R);
   const size_t sh = gemv_lds_bytes(DT, a.M, a.K);
   if (a.M == 1)
-    hipLaunchKernelGGL((gemv_row_kernel<DT, EPI, NORM, 1, R>), dim3(grid), dim3(256), sh, s, a);
+    LL_LAUNCH((gemv_row_kernel<DT, EPI, NORM, 1, R>), dim3(grid), dim3(256), sh, s, a);
   else
-    hipLaunchKernelGGL((gemv_row_kernel<DT, EPI, NORM, 4, R>), dim3(grid), dim3(256), sh, s, a);
+    LL_LAUNCH((gemv_row_kernel<DT, EPI, NORM, 4, R>), dim3(grid), dim3(256), sh, s, a);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ hipError_t launch_rope_table(float* c, float* sn, int max_pos, int hd, float the
   const size_t total = (size_t)max_pos * (hd / 2);
   int grid = (int)((total + 255) / 256);
   if (grid > 4096) grid = 4096;
-  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, s, c, sn, max_pos, hd, (double)theta);
+  LL_LAUNCH(rope_table_kernel, dim3(grid), dim3(256), 0, s, c, sn, max_pos, hd, (double)theta);
   return hipGetLastError();
 }
 
@@ -42,7 +42,7 @@ __global__ void embed_kernel(const uint8_t* table, const int32_t* ids, uint8_t* 
 hipError_t launch_embed(const void* table, const int32_t* ids, void* h, int n, int H, int vocab,
                         int dt, hipStream_t s) {
   const int row_bytes = H * (dt == DT_F32 ? 4 : 2);
-  hipLaunchKernelGGL(embed_kernel, dim3(n), dim3(256), 0, s, (const uint8_t*)table, ids, (uint8_t*)h,
+  LL_LAUNCH(embed_kernel, dim3(n), dim3(256), 0, s, (const uint8_t*)table, ids, (uint8_t*)h,
                      row_bytes, vocab);
   return hipGetLastError();
 }
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int32_
 }
 
 hipError_t launch_argmax(const float* logits, int32_t* ids, int n, int vocab, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_kernel, dim3(n), dim3(256), 0, s, logits, ids, vocab);
+  LL_LAUNCH(argmax_kernel, dim3(n), dim3(256), 0, s, logits, ids, vocab);
   return hipGetLastError();
 }
 

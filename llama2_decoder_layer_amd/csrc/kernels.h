@@ -1,6 +1,7 @@
 // Host-side launch interface between the C ABI (layer.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -103,8 +104,27 @@ enum KernelId {
   KID_ATTN_PREFILL,
   KID_COUNT
 };
-// Records the start/stop events around a launch when that kernel is armed.
+// Benchmark timer.  timer_before arms an event pair for the next launch when
+// kernel `kid` is the one being timed; the launch itself (LL_LAUNCH) hands the
+// pair to the dispatch, which records its own start and end, so the pair
+// brackets that kernel's execution and nothing else.  timer_after disarms.
+struct ArmedEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
 void timer_before(int kid, hipStream_t s);
 void timer_after(int kid, hipStream_t s);
+ArmedEvents take_armed_events();
+
+// Every kernel of the library is launched through this macro.
+#define LL_LAUNCH(kernel, grid, block, shm, stream, ...)                                      \
+  do {                                                                                        \
+    const ::ll::ArmedEvents ev_ = ::ll::take_armed_events();                                  \
+    if (ev_.start)                                                                            \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, ev_.start, ev_.stop, 0,         \
+                            __VA_ARGS__);                                                     \
+    else                                                                                      \
+      hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                      \
+  } while (0)
 
 }  // namespace ll

@@ -42,14 +42,25 @@ struct Timer {
 };
 static Timer g_timer;
 
-void timer_before(int kid, hipStream_t s) {
+static ArmedEvents g_armed = {nullptr, nullptr};
+static bool g_armed_taken = false;
+
+void timer_before(int kid, hipStream_t) {
+  g_armed = {nullptr, nullptr};
+  g_armed_taken = false;
   if (g_timer.kid != kid || g_timer.count >= g_timer.max) return;
-  (void)hipEventRecord(g_timer.ev[2 * g_timer.count], s);
+  g_armed = {g_timer.ev[2 * g_timer.count], g_timer.ev[2 * g_timer.count + 1]};
 }
-void timer_after(int kid, hipStream_t s) {
-  if (g_timer.kid != kid || g_timer.count >= g_timer.max) return;
-  (void)hipEventRecord(g_timer.ev[2 * g_timer.count + 1], s);
-  ++g_timer.count;
+ArmedEvents take_armed_events() {
+  const ArmedEvents e = g_armed;
+  if (e.start) g_armed_taken = true;
+  g_armed = {nullptr, nullptr};
+  return e;
+}
+void timer_after(int kid, hipStream_t) {
+  if (g_timer.kid == kid && g_armed_taken) ++g_timer.count;
+  g_armed = {nullptr, nullptr};
+  g_armed_taken = false;
 }
 
 // ---------------------------------------------------------------------------
@@ -473,8 +484,10 @@ int llama_layer_timer_start(int32_t kernel_id, int32_t max_launches) {
   if (kernel_id < 0 || kernel_id >= KID_COUNT || max_launches <= 0) return LL_EINVAL;
   for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
   g_timer.ev.assign(2 * (size_t)max_launches, nullptr);
+  // No system-scope fence at the events: a release to system scope writes back
+  // and invalidates caches, which would be counted as kernel time.
   for (auto& e : g_timer.ev)
-    if (hipEventCreate(&e) != hipSuccess) return LL_EHIP;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return LL_EHIP;
   g_timer.kid = kernel_id;
   g_timer.max = max_launches;
   g_timer.count = 0;

@@ -43,9 +43,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* x, const void*
 hipError_t launch_rmsnorm(int dt, const void* x, const void* gamma, void* u, int rows, int H,
                           float eps, hipStream_t s) {
   switch (dt) {
-    case DT_F32: hipLaunchKernelGGL(rmsnorm_kernel<DT_F32>, dim3(rows), dim3(256), 0, s, x, gamma, u, H, eps); break;
-    case DT_BF16: hipLaunchKernelGGL(rmsnorm_kernel<DT_BF16>, dim3(rows), dim3(256), 0, s, x, gamma, u, H, eps); break;
-    default: hipLaunchKernelGGL(rmsnorm_kernel<DT_F16>, dim3(rows), dim3(256), 0, s, x, gamma, u, H, eps); break;
+    case DT_F32: LL_LAUNCH(rmsnorm_kernel<DT_F32>, dim3(rows), dim3(256), 0, s, x, gamma, u, H, eps); break;
+    case DT_BF16: LL_LAUNCH(rmsnorm_kernel<DT_BF16>, dim3(rows), dim3(256), 0, s, x, gamma, u, H, eps); break;
+    default: LL_LAUNCH(rmsnorm_kernel<DT_F16>, dim3(rows), dim3(256), 0, s, x, gamma, u, H, eps); break;
   }
   return hipGetLastError();
 }
