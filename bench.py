@@ -114,13 +114,123 @@ def cpu_baseline_prefill(wl, stored, inp, budget_s: float) -> dict:
             "sample": f"one oracle prefill of the first {T} tokens of this workload in {el:.1f} s"}
 
 
+def cpu_baseline_stack(wl, drawn, budget_s: float) -> dict:
+    """The oracle on one layer of the stack (layer 0's weights copied back)
+    decoding at the prompt's end, plus the LM head, extrapolated to every layer."""
+    from oracle import llama_ref as R
+    import torch
+    s = wl.shape
+    f64 = lambda t: t.detach().to(torch.float64).cpu().numpy()
+    cfg = R.LayerConfig(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.eps,
+                        s.rope_theta)
+    w = R.LayerWeights(**{k: f64(v) for k, v in drawn["layers"][0].items()})
+    rng = np.random.default_rng(0)
+    kc = rng.standard_normal((1, s.n_kv_heads, wl.s_max, s.head_dim))
+    vc = rng.standard_normal(kc.shape)
+    x = rng.standard_normal((1, s.hidden))
+    ctx = np.array([wl.prompt])
+    n, t0 = 0, time.perf_counter()
+    while True:
+        R.layer_decode(cfg, w, x, kc, vc, ctx)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    t_layer = el / n
+    w_lm, gf = f64(drawn["w_lm"]), f64(drawn["final_norm"])
+    t1 = time.perf_counter()
+    R.greedy(R.lm_head(x, gf, w_lm, s.eps))
+    t_head = time.perf_counter() - t1
+    per_tok = wl.n_layers * t_layer + t_head
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"extrapolation: {n} oracle decode calls of layer 0 at context {wl.prompt} "
+                      f"({t_layer * 1e3:.0f} ms each) x {wl.n_layers} layers + one LM head "
+                      f"({t_head * 1e3:.0f} ms)"}
+
+
+def bench_stack(args, wl):
+    """The 80-layer stack at batch 1: a warm-up generation (prefill and `warmup`
+    decode steps), then a fresh generation whose prefill (time to first token)
+    and first `steps` decode steps are timed.  value = decode tokens/s."""
+    import torch
+    from llama2_decoder_layer_amd import binding as B
+    from llama2_decoder_layer_amd import synth as S
+    from llama2_decoder_layer_amd.stack import device_stack
+    s = wl.shape
+    steps = min(args.steps, wl.new_tokens)
+    warm = min(args.warmup, wl.new_tokens)
+    print(f"[bench] drawing {wl.n_layers} layers on the device", file=sys.stderr, flush=True)
+    drawn = S.draw_stack_device(wl)
+    stack = device_stack(s, wl.act_dtype, wl.kv_dtype, wl.s_max, drawn)
+    prompt = torch.from_numpy(drawn["prompt"]).cuda()
+    print(f"[bench] warm-up: prefill + {warm} decode steps", file=sys.stderr, flush=True)
+    g = stack.begin(prompt, wl.new_tokens, wl.s_max)
+    g.prefill()
+    for i in range(warm):
+        g.decode(i)
+    torch.cuda.synchronize()
+    del g
+    g = stack.begin(prompt, wl.new_tokens, wl.s_max)
+    torch.cuda.synchronize()
+    print(f"[bench] timing prefill + {steps} decode steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    g.prefill()
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    kid = B.kernel_id("gemv_gate_up")
+    B.llama_layer_timer_start(kid, wl.n_layers * steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        g.decode(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kms, kn = B.llama_layer_timer_stop()
+    ms_tok = el * 1e3 / steps
+    act_b = S.DTYPE_BYTES[wl.act_dtype]
+    kv_b = S.DTYPE_BYTES[wl.kv_dtype]
+    ctx_mean = wl.prompt + (steps - 1) / 2
+    per_layer = decode_bytes(s, [ctx_mean], act_b, kv_b)
+    head = wl.vocab * s.hidden * act_b + s.hidden * act_b
+    tok_bytes = wl.n_layers * per_layer["total"] + head
+    gbps = tok_bytes / (ms_tok / 1e3) / 1e9
+    kavg_s = kms / 1e3 / max(kn, 1)
+    ach = per_layer["gemv_gate_up"] / kavg_s / 1e9
+    fl = wl.n_layers * prefill_flops(s, wl.prompt)["total"]
+    out = {"metric": METRIC, "value": steps / el, "unit": "tokens/s", "n_gpus": 1,
+           "steps": steps, "warmup": warm, "ms_per_step": ms_tok, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": wl.act_dtype,
+           "data": "synthetic (device-drawn seeded weights; see synth.py)",
+           "stack_hbm": {"bytes_per_token": int(tok_bytes), "GBps": gbps,
+                         "frac_of_peak": gbps / HBM_PEAK_GBPS},
+           "prefill": {"tokens": wl.prompt, "time_to_first_token_ms": t_prefill * 1e3,
+                       "flops": fl, "TFLOPs": fl / t_prefill / 1e12,
+                       "frac_of_peak": fl / t_prefill / 1e12 / BF16_PEAK_TFLOPS},
+           "roofline": {"bound": "hbm", "kernel": "gemv_gate_up", "achieved": ach,
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                        "traffic": None,
+                        "algorithmic_bytes_per_launch": per_layer["gemv_gate_up"],
+                        "avg_launch_us": kavg_s * 1e6, "launches_timed": kn},
+           "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": s.hidden,
+                      "n_heads": s.n_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
+                      "intermediate": s.intermediate, "vocab": wl.vocab, "batch": 1,
+                      "prompt": wl.prompt, "kv_dtype": wl.kv_dtype},
+           "ids_head": [int(i) for i in g.ids[:8].cpu()]}
+    if args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    else:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_stack(wl, drawn, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_7b_b1_ctx4096",
-                    choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096"])
+                    choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
+                             "stack_70b_80l"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -139,6 +249,9 @@ def main():
     from llama2_decoder_layer_amd import synth as S
 
     wl = S.WORKLOADS[args.workload]
+    if wl.phase == "stack":
+        bench_stack(args, wl)
+        return
     s = wl.shape
     act, kvd = wl.act_dtype, wl.kv_dtype
     act_b, kv_b = S.DTYPE_BYTES[act], S.DTYPE_BYTES[kvd]

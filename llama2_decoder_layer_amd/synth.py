@@ -200,6 +200,12 @@ def inputs_seed(k: int) -> np.random.SeedSequence:
     return np.random.SeedSequence(2000 + k)
 
 
+def draw_prompt(w: Workload) -> np.ndarray:
+    """Prompt ids ~ U{0 .. vocab-1}, int32."""
+    rng = np.random.Generator(np.random.PCG64(inputs_seed(w.index)))
+    return rng.integers(0, w.vocab, size=w.prompt, dtype=np.int64).astype(np.int32)
+
+
 def draw_stack(w: Workload) -> dict:
     """Stack: layers, embedding table, final gain, LM head and the prompt."""
     ss = weights_seed(w.index)
@@ -208,10 +214,52 @@ def draw_stack(w: Workload) -> dict:
     embed = normal(kids[w.n_layers], (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype)
     w_lm = normal(kids[w.n_layers + 1], (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype)
     final_norm = to_storage(np.ones(w.shape.hidden, np.float32), w.act_dtype)
-    rng = np.random.Generator(np.random.PCG64(inputs_seed(w.index)))
-    prompt = rng.integers(0, w.vocab, size=w.prompt, dtype=np.int64)
     return dict(layers=layers, embed=embed, w_lm=w_lm, final_norm=final_norm,
-                prompt=prompt.astype(np.int32))
+                prompt=draw_prompt(w))
+
+
+# --------------------------------------------------------------------------
+# Device-side draws.  The 80-layer stack holds ~140 GB of weights: they are
+# drawn where they live, by torch's device generator (Philox, counter based)
+# keyed by (seed, tensor id), in float32 and rounded to the storage format
+# (round to nearest even).  Tests that check a layer copy its values back.
+# --------------------------------------------------------------------------
+DEVICE_TENSOR_IDS = 16        # ids per layer; the embedding and LM head follow the layers
+
+
+def device_normal(seed: int, tensor_id: int, shape, std: float, dtype: str, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * (1 << 20) + tensor_id)
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(0.0, std, generator=g)
+    if dtype == "f32":
+        return t
+    return t.to({"bf16": torch.bfloat16, "f16": torch.float16}[dtype])
+
+
+def draw_stack_device(w: Workload, device="cuda") -> dict:
+    """The stack drawn on the device: layers (dicts of tensors, gains are ones),
+    embedding table, final gain and LM head; the prompt stays a host array."""
+    import torch
+    seed = 1000 + w.index
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act_dtype]
+    shapes = layer_tensor_shapes(w.shape)
+    layers = []
+    for l in range(w.n_layers):
+        d = {name: device_normal(seed, l * DEVICE_TENSOR_IDS + i, shapes[name], WEIGHT_STD,
+                                 w.act_dtype, device)
+             for i, name in enumerate(LAYER_TENSORS)}
+        d["attn_norm"] = torch.ones(w.shape.hidden, dtype=tdt, device=device)
+        d["ffn_norm"] = torch.ones(w.shape.hidden, dtype=tdt, device=device)
+        layers.append(d)
+    base = w.n_layers * DEVICE_TENSOR_IDS
+    embed = device_normal(seed, base, (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype, device)
+    w_lm = device_normal(seed, base + 1, (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype,
+                         device)
+    final_norm = torch.ones(w.shape.hidden, dtype=tdt, device=device)
+    return dict(layers=layers, embed=embed, w_lm=w_lm, final_norm=final_norm,
+                prompt=draw_prompt(w))
 
 
 def draw_decode_inputs(ss: np.random.SeedSequence, s: Shape, batch: int, s_max: int,
