@@ -178,6 +178,30 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 acc) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS loads (global_load_lds_dwordx4): lane l of a wave writes
+// bytes [16 l, 16 l + 16) of the LDS destination, read from its own global
+// address, so no registers stage the data and no ds_write is issued.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt at their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// ---------------------------------------------------------------------------
 // Wavefront reductions (64 lanes).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

@@ -253,25 +253,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(ProjArgs a) {
 // A 32-k row slice is 64 bytes, four rows per 256-byte bank sweep: chunk c of
 // row r is stored at chunk c ^ ((r >> 2) & 3).
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
-
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt at their maxima).
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-}
-
 // Occupancy target per SIMD: 4 waves on a 256 x 256 tile hold 256 accumulator
 // registers each (one wave per SIMD); 8 waves hold 128 (two per SIMD, so one
 // wave's barrier and LDS waits overlap the other's MFMAs).  Telling the

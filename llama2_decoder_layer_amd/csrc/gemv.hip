@@ -19,6 +19,8 @@
 //  * gemv_glb: larger token counts; activation chunks come from global memory
 //    (L2) one block ahead of use.  A fused norm is not available here: the
 //    host normalises first.
+// For 16-bit formats without a fused norm, the LDS-streaming kernel of
+// gemv_dma.hip takes every case the row kernel does not.
 // Epilogues: RoPE + KV-cache append (QKV), residual add (O, down), SwiGLU
 // (gate/up, two weight matrices) or float32 logits (LM head).
 #include "common.cuh"
@@ -505,6 +507,7 @@ static hipError_t gemv_dt(int epi, const ProjArgs& a, hipStream_t s) {
     }
     return hipErrorInvalidValue;
   }
+  if (!norm && gemv_dma_supported(DT, a.M, a.K, a.N)) return launch_gemv_dma(DT, epi, a, s);
   if (gemv_fits_lds(DT, a.M, a.K)) {
     switch (epi) {
       case EPI_QKV: return norm ? gemv_lds_launch<DT, EPI_QKV, true>(a, s)

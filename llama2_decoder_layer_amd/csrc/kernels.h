@@ -36,6 +36,7 @@ struct ProjArgs {
   int nh, nkv, hd, s_max, kv_dt;
   const float* rcos;
   const float* rsin;
+  float* part;        // float32 K-split partials of the streaming projection (workspace)
 };
 
 // Decode-sized projection (M <= 32 tokens).  A fused norm (gamma != nullptr)
@@ -43,6 +44,14 @@ struct ProjArgs {
 hipError_t launch_gemv(int dt, int epi, const ProjArgs& a, hipStream_t s);
 bool gemv_fits_lds(int dt, int M, int K);
 hipError_t launch_gemm(int dt, int epi, const ProjArgs& a, hipStream_t s);
+
+// Weight-streaming projection through LDS for 16-bit formats (K % 64 == 0,
+// N % 4 == 0, M <= 32, no fused norm); launch_gemv picks it when the row
+// kernel does not apply.  Few row blocks split K; the splits' partials go to
+// a.part, which must hold gemv_dma_partial_floats(epi, N, K, M) floats.
+bool gemv_dma_supported(int dt, int M, int K, int N);
+size_t gemv_dma_partial_floats(int epi, int N, int K, int M);
+hipError_t launch_gemv_dma(int dt, int epi, const ProjArgs& a, hipStream_t s);
 
 // RMSNorm of `rows` rows of width H: u = x / sqrt(mean(x^2) + eps) * gamma.
 hipError_t launch_rmsnorm(int dt, const void* x, const void* gamma, void* u, int rows, int H,

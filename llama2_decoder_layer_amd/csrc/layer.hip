@@ -119,7 +119,7 @@ static bool wide_plan(const ll_config* c, int64_t tokens_total, bool decode) {
 }
 
 struct Layout {
-  size_t q32, pm, pl, pacc, u, q16, o, h1, a, total;
+  size_t q32, pm, pl, pacc, part, u, q16, o, h1, a, total;
   int nsplit_max;
 };
 
@@ -142,6 +142,18 @@ static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide) {
     L.pm = take(g * c->n_heads * L.nsplit_max * 4);
     L.pl = take(g * c->n_heads * L.nsplit_max * 4);
     L.pacc = take(g * c->n_heads * L.nsplit_max * c->head_dim * 4);
+    // K-split partials of the streaming projections.
+    const int H = c->hidden, I = c->intermediate;
+    const int qkv = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+    const int qd_ = c->n_heads * c->head_dim;
+    size_t pf = 0;
+    for (int m = 1; m <= g; ++m) {
+      pf = std::max(pf, gemv_dma_partial_floats(EPI_QKV, qkv, H, m));
+      pf = std::max(pf, gemv_dma_partial_floats(EPI_RESID, H, qd_, m));
+      pf = std::max(pf, gemv_dma_partial_floats(EPI_SWIGLU, I, H, m));
+      pf = std::max(pf, gemv_dma_partial_floats(EPI_RESID, H, I, m));
+    }
+    L.part = take(pf * 4);
   }
   L.o = take(bt * qd * act);
   L.h1 = take(bt * c->hidden * act);
@@ -189,8 +201,11 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
   const bool fuse_norm = gemv_fits_lds(dt, m, H);
   void* u = ws + L.u;
 
+  float* part = (float*)(ws + L.part);
+
   // 1. QKV + RMSNorm + RoPE + cache append.
   ProjArgs p = base_args(c);
+  p.part = part;
   p.w[0] = w->w_q; p.w[1] = w->w_k; p.w[2] = w->w_v;
   p.seg1 = qd; p.seg2 = qd + kd;
   p.N = qd + 2 * kd; p.K = H; p.M = m; p.tok0 = (int)tok0;
@@ -245,6 +260,7 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
 
   // 3. O projection + residual.
   ProjArgs po = base_args(c);
+  po.part = part;
   po.w[0] = w->w_o; po.seg1 = po.seg2 = H;
   po.N = H; po.K = qd; po.M = m; po.x = o; po.resid = xm; po.y = h1;
   timer_before(KID_GEMV_O, s);
@@ -253,6 +269,7 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
 
   // 4. gate/up + RMSNorm + SwiGLU.
   ProjArgs pg = base_args(c);
+  pg.part = part;
   pg.w[0] = w->w_gate; pg.w[1] = w->w_up;
   pg.N = I; pg.K = H; pg.M = m; pg.y = a;
   if (fuse_norm) {
@@ -269,6 +286,7 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
 
   // 5. down + residual.
   ProjArgs pd = base_args(c);
+  pd.part = part;
   pd.w[0] = w->w_down; pd.seg1 = pd.seg2 = H;
   pd.N = H; pd.K = I; pd.M = m; pd.x = a; pd.resid = h1; pd.y = ym;
   timer_before(KID_GEMV_DOWN, s);
