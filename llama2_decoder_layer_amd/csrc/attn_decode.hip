@@ -179,6 +179,167 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnDecodeArgs a) {
   }
 }
 
+// GQA variant for 16-bit caches with GC = 4 or 8 query heads per workgroup.
+// The scores of a 16-key tile come from v_mfma_f32_16x16x32 with K in the A
+// layout (lane: key r16, dims 32s + 8(l/16) of slice s, loaded straight from
+// the cache as 64-byte row pieces) and the group's queries in the B layout
+// (head r16; columns past GC are zero), so no cross-lane dot-product
+// reductions are needed.  Each of the 4 waves scores KW = 16 TW keys; the
+// workgroup's max comes through LDS, P = 2^(S - max) goes to LDS as
+// [key][head], and P V runs on the VALU with each lane holding 8 dims of its
+// V rows (V would need a transpose to be an MFMA operand).  Queries are
+// rounded to the cache format for the MFMA.  Output: the same partials as
+// attn_split_kernel, one split per CH = 64 TW keys.
+template <int KVDT, int HD, int GC, int TW>
+__global__ __launch_bounds__(256) void attn_gqa_kernel(AttnDecodeArgs a) {
+  typedef typename Elt<KVDT>::T T;
+  constexpr int NS = HD / 32;   // 32-dim slices: MFMAs per 16-key tile
+  constexpr int KW = 16 * TW;   // keys per wave
+  constexpr int CH = 4 * KW;    // keys per workgroup
+  constexpr int DGN = HD / 8;   // 8-dim groups of a row
+  constexpr int KG = 64 / DGN;  // V rows per wave load instruction
+  constexpr int KPL = KW / KG;  // V rows per lane
+  const int split = blockIdx.x;
+  const int g = a.nh / a.nkv;
+  const int per_kv = g / GC;
+  const int j = blockIdx.y / per_kv;
+  const int h0 = j * g + (blockIdx.y - j * per_kv) * GC;
+  const int n = blockIdx.z;
+  int b;
+  const int pos = query_position(a, n, &b);
+  const int k_lo = split * CH;
+  const int k_hi = min(k_lo + CH, pos + 1);
+  if (k_lo >= k_hi) return;  // past this query's context: not counted, not merged
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int kw0 = k_lo + wave * KW;
+  const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD;
+  const T* kp = reinterpret_cast<const T*>(a.kc) + head_off;
+  const T* vp = reinterpret_cast<const T*>(a.vc) + head_off;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  u32x4 kr[TW][NS];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int key = kw0 + 16 * t + r16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kr[t][s] = key < k_hi ? ld16(kp + (size_t)key * HD + 32 * s + 8 * g4) : zero;
+  }
+  const int vdg = lane % DGN, vkey = lane / DGN;
+  u32x4 vr[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int key = kw0 + vkey + KG * i;
+    vr[i] = key < k_hi ? ld16(vp + (size_t)key * HD + 8 * vdg) : zero;
+  }
+
+  const float qscale = 1.44269504088896341f / sqrtf((float)HD);
+  u32x4 qb[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (r16 < GC) {
+      const float* qp = a.q + ((size_t)n * a.nh + h0 + r16) * HD + 32 * s + 8 * g4;
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qp);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qp + 4);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = q0[e] * qscale;
+        f[e + 4] = q1[e] * qscale;
+      }
+      qb[s] = pack16<KVDT>(f);
+    } else {
+      qb[s] = zero;
+    }
+  }
+
+  // Scores: lane holds head r16, keys 16t + 4 g4 + i of its wave.
+  f32x4 sc[TW];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) c = mfma16_chunk<KVDT>(kr[t][s], qb[s], c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kw0 + 16 * t + 4 * g4 + i >= k_hi) c[i] = -INFINITY;
+      mx = fmaxf(mx, c[i]);
+    }
+    sc[t] = c;
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  __shared__ float s_mx[4][16], s_l[4][16];
+  __shared__ float s_p[CH][GC];
+  __shared__ float s_acc[4][GC][HD];
+  if (g4 == 0) s_mx[wave][r16] = mx;
+  __syncthreads();
+  // Wave 0 always holds a valid key, so the workgroup maximum is finite.
+  const float M = fmaxf(fmaxf(s_mx[0][r16], s_mx[1][r16]), fmaxf(s_mx[2][r16], s_mx[3][r16]));
+  float lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = exp2f(sc[t][i] - M);
+      lsum += p;
+      if (r16 < GC) s_p[wave * KW + 16 * t + 4 * g4 + i][r16] = p;
+    }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (g4 == 0) s_l[wave][r16] = lsum;
+  __syncthreads();
+
+  // P V over this lane's V rows (rows past the context are zero, as is P).
+  float acc[GC][8];
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int kl = wave * KW + vkey + KG * i;
+    float vf[8];
+    unpack16<KVDT>(vr[i], vf);
+    float p[GC];
+#pragma unroll
+    for (int h = 0; h < GC; h += 4) {
+      const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[kl][h]);
+      p[h] = p4[0]; p[h + 1] = p4[1]; p[h + 2] = p4[2]; p[h + 3] = p4[3];
+    }
+#pragma unroll
+    for (int h = 0; h < GC; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += p[h] * vf[e];
+  }
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int o = DGN; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+  if (lane < DGN) {
+#pragma unroll
+    for (int h = 0; h < GC; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wave][h][vdg * 8 + e] = acc[h][e];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < GC * HD; idx += 256) {
+    const int h = idx / HD, d = idx - h * HD;
+    const float v = s_acc[0][h][d] + s_acc[1][h][d] + s_acc[2][h][d] + s_acc[3][h][d];
+    a.part_acc[(((size_t)n * a.nh + h0 + h) * a.nsplit + split) * HD + d] = v;
+  }
+  if (tid < GC) {
+    const size_t pi = ((size_t)n * a.nh + h0 + tid) * a.nsplit + split;
+    a.part_m[pi] = fmaxf(fmaxf(s_mx[0][tid], s_mx[1][tid]), fmaxf(s_mx[2][tid], s_mx[3][tid]));
+    a.part_l[pi] = s_l[0][tid] + s_l[1][tid] + s_l[2][tid] + s_l[3][tid];
+  }
+}
+
 // Merge of the splits of one (query, head group).  The 256 threads form
 // HD/4 groups of 4 consecutive dims x 1024/HD split groups; each sums every
 // (1024/HD)-th split with float4 loads, and the split groups meet in LDS.
@@ -255,11 +416,28 @@ static hipError_t split_launch_kpt(const AttnDecodeArgs& a, dim3 grid, hipStream
   return hipGetLastError();
 }
 
+template <int KVDT, int HD, int GC>
+static hipError_t gqa_launch_tw(const AttnDecodeArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.chunk / 64) {
+    case 1: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 4>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int KVDT, int HD>
 static hipError_t split_launch(const AttnDecodeArgs& a, hipStream_t s) {
   const int g = a.nh / a.nkv;
   const int gc = attn_heads_per_group(g);
   dim3 grid(a.nsplit, a.nkv * (g / gc), a.nq);
+  if constexpr (KVDT != DT_F32) {
+    if (attn_uses_gqa_kernel(a.kv_dt, g)) {
+      if (gc == 8) return gqa_launch_tw<KVDT, HD, 8>(a, grid, s);
+      return gqa_launch_tw<KVDT, HD, 4>(a, grid, s);
+    }
+  }
   switch (gc) {
     case 8: return split_launch_kpt<KVDT, HD, 8>(a, grid, s);
     case 4: return split_launch_kpt<KVDT, HD, 4>(a, grid, s);
@@ -270,13 +448,28 @@ static hipError_t split_launch(const AttnDecodeArgs& a, hipStream_t s) {
 
 int attn_heads_per_group(int g) { return (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1; }
 
-int attn_pick_chunk(int hd, int max_keys, int queries, int nkv, int g) {
+bool attn_uses_gqa_kernel(int kv_dt, int g) {
+  return kv_dt != DT_F32 && attn_heads_per_group(g) >= 4;
+}
+
+int attn_pick_chunk(int hd, int max_keys, int queries, int nkv, int g, int kv_dt) {
+  const int gc = attn_heads_per_group(g);
+  const int groups = nkv * (g / gc);
+  if (attn_uses_gqa_kernel(kv_dt, g)) {
+    // Chunk 64, 128 or 256 keys: the largest that still gives >= 2048 workgroups.
+    int tw = 4;
+    while (tw > 1 && (int64_t)((max_keys + 64 * tw - 1) / (64 * tw)) * queries * groups < 2048)
+      tw >>= 1;
+    while ((max_keys + 64 * tw - 1) / (64 * tw) > ATTN_MAX_SPLITS) {
+      if (tw >= 4) return -1;
+      tw *= 2;
+    }
+    return 64 * tw;
+  }
   // Keys per thread 2..8 (at most 4 with 8 heads per group), chunk = kpt * 256 / (hd / 8):
   // the largest chunk that still gives >= 2048 workgroups, and never more than
   // ATTN_MAX_SPLITS splits (the merge keeps one weight per split in LDS).
   const int kpi = 256 / (hd / 8);
-  const int gc = attn_heads_per_group(g);
-  const int groups = nkv * (g / gc);
   const int kpt_max = gc >= 8 ? 4 : 8;
   int pick = 2;
   for (int kpt = kpt_max; kpt >= 2; kpt >>= 1) {

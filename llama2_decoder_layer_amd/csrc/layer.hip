@@ -231,7 +231,8 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
   at.T = T; at.max_ctx = max_ctx; at.nq = m; at.nh = c->n_heads; at.nkv = c->n_kv_heads;
   at.hd = c->head_dim; at.s_max = s_max; at.kv_dt = c->kv_dtype; at.act_dt = dt;
   const int max_keys = ctx_len ? max_ctx + 1 : start_pos + T;
-  at.chunk = attn_pick_chunk(c->head_dim, max_keys, m, c->n_kv_heads, c->n_heads / c->n_kv_heads);
+  at.chunk = attn_pick_chunk(c->head_dim, max_keys, m, c->n_kv_heads, c->n_heads / c->n_kv_heads,
+                             c->kv_dtype);
   if (at.chunk < 0) return LL_EUNSUPPORTED;
   at.nsplit = (max_keys + at.chunk - 1) / at.chunk;
   if (at.nsplit > L.nsplit_max) return LL_EWORKSPACE;
