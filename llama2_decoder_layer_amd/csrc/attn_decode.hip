@@ -184,21 +184,29 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnDecodeArgs a) {
 // layout (lane: key r16, dims 32s + 8(l/16) of slice s, loaded straight from
 // the cache as 64-byte row pieces) and the group's queries in the B layout
 // (head r16; columns past GC are zero), so no cross-lane dot-product
-// reductions are needed.  Each of the 4 waves scores KW = 16 TW keys; the
-// workgroup's max comes through LDS, P = 2^(S - max) goes to LDS as
-// [key][head], and P V runs on the VALU with each lane holding 8 dims of its
-// V rows (V would need a transpose to be an MFMA operand).  Queries are
-// rounded to the cache format for the MFMA.  Output: the same partials as
-// attn_split_kernel, one split per CH = 64 TW keys.
-template <int KVDT, int HD, int GC, int TW>
-__global__ __launch_bounds__(256) void attn_gqa_kernel(AttnDecodeArgs a) {
+// reductions are needed.  P V runs on the VALU with each lane holding 8 dims
+// of its V rows (V would need a transpose to be an MFMA operand); P and the
+// rescale factors reach those lanes through a per-wave LDS area.
+//
+// Each wave streams its own keys, 16 per iteration (keys k_lo + 64 it +
+// 16 wave + [0, 16)), with an online softmax, so the waves never wait for each
+// other until the end, where their (max, sum, acc) are combined in LDS.  The
+// next iteration's K rows are requested right after the scores consume the
+// current ones, and its V rows right after P V.  Queries are rounded to the
+// cache format for the MFMA.  Output: the same partials as attn_split_kernel,
+// one split per CH = 64 NIT keys.
+template <int KVDT, int HD, int GC, int NIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_gqa_kernel(AttnDecodeArgs a) {
   typedef typename Elt<KVDT>::T T;
   constexpr int NS = HD / 32;   // 32-dim slices: MFMAs per 16-key tile
-  constexpr int KW = 16 * TW;   // keys per wave
-  constexpr int CH = 4 * KW;    // keys per workgroup
+  constexpr int TW = 1;         // 16-key tiles per wave and iteration
+  constexpr int KW = 16 * TW;   // keys per wave and iteration
+  constexpr int WI = 4 * KW;    // keys per workgroup and iteration
+  constexpr int CH = WI * NIT;  // keys per workgroup
   constexpr int DGN = HD / 8;   // 8-dim groups of a row
   constexpr int KG = 64 / DGN;  // V rows per wave load instruction
-  constexpr int KPL = KW / KG;  // V rows per lane
+  constexpr int KPL = KW / KG;  // V rows per lane and iteration
   const int split = blockIdx.x;
   const int g = a.nh / a.nkv;
   const int per_kv = g / GC;
@@ -210,30 +218,41 @@ __global__ __launch_bounds__(256) void attn_gqa_kernel(AttnDecodeArgs a) {
   const int k_lo = split * CH;
   const int k_hi = min(k_lo + CH, pos + 1);
   if (k_lo >= k_hi) return;  // past this query's context: not counted, not merged
+  const int nit = (k_hi - k_lo + WI - 1) / WI;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int kw0 = k_lo + wave * KW;
+  const int vdg = lane % DGN, vkey = lane / DGN;
   const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD;
   const T* kp = reinterpret_cast<const T*>(a.kc) + head_off;
   const T* vp = reinterpret_cast<const T*>(a.vc) + head_off;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  // Offsets within one head's rows fit 32 bits: loads take a uniform base
+  // plus a 32-bit lane offset.
+  const uint32_t ko = 8u * g4, vo = 8u * vdg;  // element offsets within a row
 
-  u32x4 kr[TW][NS];
+  // Rows past the chunk's end read the last valid row (finite values whose
+  // scores are masked and whose P is zero), so the loads need no branches.
+  u32x4 kr[TW][NS], vr[KPL];
+  auto load_k = [&](int it) {
+    const int kb = k_lo + WI * it + KW * wave;
 #pragma unroll
-  for (int t = 0; t < TW; ++t) {
-    const int key = kw0 + 16 * t + r16;
+    for (int t = 0; t < TW; ++t) {
+      const uint32_t key = (uint32_t)min(kb + 16 * t + r16, k_hi - 1);
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kr[t][s] = key < k_hi ? ld16(kp + (size_t)key * HD + 32 * s + 8 * g4) : zero;
-  }
-  const int vdg = lane % DGN, vkey = lane / DGN;
-  u32x4 vr[KPL];
+      for (int s = 0; s < NS; ++s) kr[t][s] = ld16(kp + (key * HD + 32 * s + ko));
+    }
+  };
+  auto load_v = [&](int it) {
+    const int kb = k_lo + WI * it + KW * wave;
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const int key = kw0 + vkey + KG * i;
-    vr[i] = key < k_hi ? ld16(vp + (size_t)key * HD + 8 * vdg) : zero;
-  }
+    for (int i = 0; i < KPL; ++i) {
+      const uint32_t key = (uint32_t)min(kb + vkey + KG * i, k_hi - 1);
+      vr[i] = ld16(vp + (key * HD + vo));
+    }
+  };
+  load_k(0);
+  load_v(0);
 
   const float qscale = 1.44269504088896341f / sqrtf((float)HD);
   u32x4 qb[NS];
@@ -255,88 +274,128 @@ __global__ __launch_bounds__(256) void attn_gqa_kernel(AttnDecodeArgs a) {
     }
   }
 
-  // Scores: lane holds head r16, keys 16t + 4 g4 + i of its wave.
-  f32x4 sc[TW];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < TW; ++t) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) c = mfma16_chunk<KVDT>(kr[t][s], qb[s], c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kw0 + 16 * t + 4 * g4 + i >= k_hi) c[i] = -INFINITY;
-      mx = fmaxf(mx, c[i]);
-    }
-    sc[t] = c;
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  __shared__ float s_mx[4][16], s_l[4][16];
-  __shared__ float s_p[CH][GC];
+  __shared__ float s_p[4][KW][GC];   // per wave: P of the current iteration
+  __shared__ float s_alpha[4][GC];   // per wave: rescale of the running sums
+  __shared__ float s_m[4][GC], s_l[4][GC];
   __shared__ float s_acc[4][GC][HD];
-  if (g4 == 0) s_mx[wave][r16] = mx;
-  __syncthreads();
-  // Wave 0 always holds a valid key, so the workgroup maximum is finite.
-  const float M = fmaxf(fmaxf(s_mx[0][r16], s_mx[1][r16]), fmaxf(s_mx[2][r16], s_mx[3][r16]));
-  float lsum = 0.f;
-#pragma unroll
-  for (int t = 0; t < TW; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(sc[t][i] - M);
-      lsum += p;
-      if (r16 < GC) s_p[wave * KW + 16 * t + 4 * g4 + i][r16] = p;
-    }
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (g4 == 0) s_l[wave][r16] = lsum;
-  __syncthreads();
 
-  // P V over this lane's V rows (rows past the context are zero, as is P).
+  float m_run = -INFINITY;  // running max of head r16 over this wave's keys
+  float l_run = 0.f;        // this lane's share of the running sum
   float acc[GC][8];
 #pragma unroll
   for (int h = 0; h < GC; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  for (int it = 0; it < nit; ++it) {
+    const int kb = k_lo + WI * it + KW * wave;
+    // Scores: lane holds head r16, keys kb + 16t + 4 g4 + i.
+    f32x4 sc[TW];
+    float mt = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const int kl = wave * KW + vkey + KG * i;
-    float vf[8];
-    unpack16<KVDT>(vr[i], vf);
-    float p[GC];
+    for (int t = 0; t < TW; ++t) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) c = mfma16_chunk<KVDT>(kr[t][s], qb[s], c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kb + 16 * t + 4 * g4 + i >= k_hi) c[i] = -INFINITY;
+        mt = fmaxf(mt, c[i]);
+      }
+      sc[t] = c;
+    }
+    if (it + 1 < nit) load_k(it + 1);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    // No valid key yet for this wave: keep everything at zero.
+    const bool none = (m_new == -INFINITY);
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sc[t][i] - m_new);
+        ls += p;
+        if (r16 < GC) s_p[wave][16 * t + 4 * g4 + i][r16] = p;
+      }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    if (g4 == 0 && r16 < GC) s_alpha[wave][r16] = alpha;
+    // (This wave's LDS writes above are seen by its reads below: one wave's
+    // LDS instructions complete in order.)
+    float al[GC];
 #pragma unroll
     for (int h = 0; h < GC; h += 4) {
-      const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[kl][h]);
-      p[h] = p4[0]; p[h + 1] = p4[1]; p[h + 2] = p4[2]; p[h + 3] = p4[3];
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&s_alpha[wave][h]);
+      al[h] = a4[0]; al[h + 1] = a4[1]; al[h + 2] = a4[2]; al[h + 3] = a4[3];
     }
 #pragma unroll
     for (int h = 0; h < GC; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += p[h] * vf[e];
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      float vf[8];
+      unpack16<KVDT>(vr[i], vf);
+      float p[GC];
+#pragma unroll
+      for (int h = 0; h < GC; h += 4) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[wave][vkey + KG * i][h]);
+        p[h] = p4[0]; p[h + 1] = p4[1]; p[h + 2] = p4[2]; p[h + 3] = p4[3];
+      }
+#pragma unroll
+      for (int h = 0; h < GC; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += p[h] * vf[e];
+      // Bounds how far the scheduler hoists the P reads and V unpacks (each
+      // key's 16 values would otherwise stay live at once).
+      if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (it + 1 < nit) load_v(it + 1);
   }
+
+  // This wave's totals: acc over the lanes holding the same dims, l over the
+  // four lanes of each head.
 #pragma unroll
   for (int h = 0; h < GC; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
       for (int o = DGN; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
   if (lane < DGN) {
 #pragma unroll
     for (int h = 0; h < GC; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) s_acc[wave][h][vdg * 8 + e] = acc[h][e];
   }
+  if (g4 == 0 && r16 < GC) {
+    s_m[wave][r16] = m_run;
+    s_l[wave][r16] = l_run;
+  }
   __syncthreads();
+  // Combine the waves (wave 0 always holds a valid key, so M is finite).
   for (int idx = tid; idx < GC * HD; idx += 256) {
     const int h = idx / HD, d = idx - h * HD;
-    const float v = s_acc[0][h][d] + s_acc[1][h][d] + s_acc[2][h][d] + s_acc[3][h][d];
+    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_m[w][h] != -INFINITY) v += exp2f(s_m[w][h] - M) * s_acc[w][h][d];
     a.part_acc[(((size_t)n * a.nh + h0 + h) * a.nsplit + split) * HD + d] = v;
   }
   if (tid < GC) {
+    const float M = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_m[w][tid] != -INFINITY) l += exp2f(s_m[w][tid] - M) * s_l[w][tid];
     const size_t pi = ((size_t)n * a.nh + h0 + tid) * a.nsplit + split;
-    a.part_m[pi] = fmaxf(fmaxf(s_mx[0][tid], s_mx[1][tid]), fmaxf(s_mx[2][tid], s_mx[3][tid]));
-    a.part_l[pi] = s_l[0][tid] + s_l[1][tid] + s_l[2][tid] + s_l[3][tid];
+    a.part_m[pi] = M;
+    a.part_l[pi] = l;
   }
 }
 
@@ -419,9 +478,10 @@ static hipError_t split_launch_kpt(const AttnDecodeArgs& a, dim3 grid, hipStream
 template <int KVDT, int HD, int GC>
 static hipError_t gqa_launch_tw(const AttnDecodeArgs& a, dim3 grid, hipStream_t s) {
   switch (a.chunk / 64) {
-    case 1: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 2>), grid, dim3(256), 0, s, a); break;
     case 4: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 8>), grid, dim3(256), 0, s, a); break;
+    case 16: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 16>), grid, dim3(256), 0, s, a); break;
+    case 32: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 32>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -456,15 +516,18 @@ int attn_pick_chunk(int hd, int max_keys, int queries, int nkv, int g, int kv_dt
   const int gc = attn_heads_per_group(g);
   const int groups = nkv * (g / gc);
   if (attn_uses_gqa_kernel(kv_dt, g)) {
-    // Chunk 64, 128 or 256 keys: the largest that still gives >= 2048 workgroups.
-    int tw = 4;
-    while (tw > 1 && (int64_t)((max_keys + 64 * tw - 1) / (64 * tw)) * queries * groups < 2048)
-      tw >>= 1;
-    while ((max_keys + 64 * tw - 1) / (64 * tw) > ATTN_MAX_SPLITS) {
-      if (tw >= 4) return -1;
-      tw *= 2;
+    // Chunk 256, 512, 1024 or 2048 keys: the largest that still gives >= 512
+    // workgroups (counted at the longest context).  Longer chunks mean fewer
+    // partials to merge and fewer per-workgroup tails; measured on the 70B
+    // batch-32 decode, 2048 beats both 1024 and 4096.
+    int nit = 8;
+    while (nit > 1 && (int64_t)((max_keys + 256 * nit - 1) / (256 * nit)) * queries * groups < 512)
+      nit >>= 1;
+    while ((max_keys + 256 * nit - 1) / (256 * nit) > ATTN_MAX_SPLITS) {
+      if (nit >= 8) return -1;
+      nit *= 2;
     }
-    return 64 * tw;
+    return 256 * nit;
   }
   // Keys per thread 2..8 (at most 4 with 8 heads per group), chunk = kpt * 256 / (hd / 8):
   // the largest chunk that still gives >= 2048 workgroups, and never more than

@@ -76,13 +76,13 @@ struct AttnDecodeArgs {
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
 // Query heads served per workgroup for a GQA group of g heads.
 int attn_heads_per_group(int g);
-// Keys per split for the launch (one of 2, 4 or 8 x 256/(hd/8); 64, 128 or 256
+// Keys per split for the launch (one of 2, 4 or 8 x 256/(hd/8); 256 to 2048
 // for the GQA kernel), or -1 when
 // the context needs more than ATTN_MAX_SPLITS splits of the largest chunk.
 constexpr int ATTN_MAX_SPLITS = 1024;
 int attn_pick_chunk(int hd, int max_keys, int queries, int nkv, int g, int kv_dt);
 // 16-bit caches with 4 or 8 query heads per group take the MFMA-score kernel
-// (chunks of 64, 128 or 256 keys).
+// (chunks of 256 to 2048 keys).
 bool attn_uses_gqa_kernel(int kv_dt, int g);
 // Smallest chunk attn_pick_chunk returns (sizes the workspace).
 inline int attn_min_chunk(int hd) { return 2 * (256 / (hd / 8)); }
