@@ -205,13 +205,206 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   }
 }
 
+// head_dim 128: the same blocking, but K and V tiles move global -> LDS by
+// global_load_lds into a two-stage ring (tile t+1 loads while tile t is used)
+// and V stays in its [key][dim] layout.  The A operand of O^T = V^T P^T is read
+// with ds_read_b64_tr_b16, which transposes 16-bit data across each group of 16
+// lanes: when lane i = 4e + q of a group reads the 4 elements at (row R + e,
+// col C + 4q), lane j of the group receives rows R..R+3 of col C + j.  Two
+// such reads give a lane the 8 keys its MFMA k-group needs for one dim.
+// Swizzles (16-byte chunk c of row r stored at chunk c ^ f(r)): K uses
+// f = r & 15 (16 rows of one b128 read on distinct banks); V uses
+// f = 4 (r & 3) (the 4 rows x 64 bytes of 32 lanes' transposed reads cover all
+// 64 banks once).  The DMA writes the swizzled layout by permuting each lane's
+// global address.
+template <int DT>
+__global__ __launch_bounds__(256) void attn_prefill_tr_kernel(AttnPrefillArgs a) {
+  typedef typename Elt<DT>::T ET;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  constexpr int HD = 128;
+  constexpr int ROWB = HD * 2;                   // bytes per key row
+  constexpr int TILE_B = PKV * ROWB;             // one K or V tile: 16 KB
+  constexpr int STAGE_B = 2 * TILE_B;            // K then V
+  // One LDS object (a second one gives the accesses alias scopes, and the
+  // wait-count pass then waits for every outstanding DMA before each read).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const int nqb = gridDim.x;
+  const int qb = nqb - 1 - blockIdx.x;  // heavy blocks first
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int j = h / (a.nh / a.nkv);
+  const int T = a.T;
+
+  const int q_first = qb * PQ;
+  const int q_last = min(q_first + PQ, T) - 1;
+  const int kv_end = a.start_pos + q_last + 1;       // keys [0, kv_end) are needed
+  const int ntiles = (kv_end + PKV - 1) / PKV;
+
+  const int wq0 = q_first + wave * 32;
+  const int w_last_pos = a.start_pos + min(wq0 + 31, T - 1);
+  const int my_t = wq0 + l32;
+  const int my_pos = a.start_pos + my_t;
+
+  const ET* qp = reinterpret_cast<const ET*>(a.q) + (((size_t)b * a.nh + h) * T + (my_t < T ? my_t : 0)) * HD;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 qf[HD / 16];
+#pragma unroll
+  for (int s = 0; s < HD / 16; ++s) qf[s] = (my_t < T) ? ld16(qp + s * 16 + h2 * 8) : zero;
+
+  const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD;
+  const ET* kbase = reinterpret_cast<const ET*>(a.kc) + head_off;
+  const ET* vbase = reinterpret_cast<const ET*>(a.vc) + head_off;
+
+  // DMA: instruction i of wave w fills rows 16w + 4i + (lane >> 4), physical
+  // chunk lane & 15.  Rows past kv_end read the last needed row (finite; those
+  // keys are masked).
+  const int rsub = lane >> 4, pch = lane & 15;
+  const int vcol = (pch ^ (4 * rsub)) * 8;  // (16w + 4i + rsub) & 3 == rsub
+  auto issue = [&](int buf, int key0) {
+    uint8_t* kb = lds + buf * STAGE_B;
+    uint8_t* vb = kb + TILE_B;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + rsub;
+      const int key = min(key0 + r, kv_end - 1);
+      const int kcol = (pch ^ (r & 15)) * 8;
+      dma16(kbase + (size_t)key * HD + kcol, kb + (16 * wave + 4 * i) * ROWB);
+      dma16(vbase + (size_t)key * HD + vcol, vb + (16 * wave + 4 * i) * ROWB);
+    }
+  };
+
+  f32x16 oacc[HD / 32];
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float qk_scale = 1.44269504088896341f / sqrtf((float)HD);
+
+  // Transposed-read addresses (bytes within a V tile) for MFMA (kb, hf, d):
+  // group gi = lane >> 4 covers dims d*32 + (gi & 1)*16 + [0, 16) and keys
+  // kb*32 + hf*16 + (gi >> 1)*4 (+8 for the second read).
+  const int gi = lane >> 4, ii = lane & 15;
+  const int tr_row = (gi >> 1) * 4 + (ii >> 2);            // + kb*32 + hf*16 (+8)
+  const int tr_col = (gi & 1) * 16 + 4 * (ii & 3);         // + d*32
+  // (row & 3) == (ii >> 2) for every read, so the swizzle is fixed per lane.
+  auto tr_off = [&](int row_add, int d) {
+    const int row = tr_row + row_add;
+    const int col = d * 32 + tr_col;
+    return row * ROWB + (((col >> 3) ^ (4 * (ii >> 2))) << 4) + ((col >> 2) & 1) * 8;
+  };
+
+  issue(0, 0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int key0 = tile * PKV;
+    wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();  // tile landed everywhere; the other buffer is free
+    __builtin_amdgcn_sched_barrier(0);
+    if (tile + 1 < ntiles) issue((tile + 1) & 1, key0 + PKV);
+    if (key0 > w_last_pos) continue;  // every key of this tile is in this wave's future
+    const uint8_t* kt = lds + (tile & 1) * STAGE_B;
+    const uint8_t* vt = kt + TILE_B;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < HD / 16; ++s) {
+      const int ch = s * 2 + h2;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kr = kb * 32 + l32;
+        const u32x4 kf = ld16(kt + kr * ROWB + ((ch ^ (kr & 15)) << 4));
+        sacc[kb] = mfma32<DT>(kf, qf[s], sacc[kb]);
+      }
+    }
+    const bool need_mask = key0 + PKV - 1 > a.start_pos + wq0;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float sv = sacc[kb][i] * qk_scale;
+        if (need_mask) {
+          const int key = key0 + kb * 32 + (i >> 2) * 8 + h2 * 4 + (i & 3);
+          if (key > my_pos) sv = -INFINITY;
+        }
+        sacc[kb][i] = sv;
+        mt = fmaxf(mt, sv);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2f(sacc[kb][i] - m_use);
+        sacc[kb][i] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32, 64);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+
+    // O^T += V^T P^T.  MFMA (kb, hf) covers keys kb*32 + hf*16 + (e/4)*8 + h2*4 + e%4.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float pf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = sacc[kb][hf * 8 + e];
+        const u32x4 pb = pack16<DT>(pf);
+#pragma unroll
+        for (int d = 0; d < HD / 32; ++d) {
+          const int base = kb * 32 + hf * 16;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(vt + tr_off(base, d)));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(vt + tr_off(base + 8, d)));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2v = __builtin_bit_cast(u32x2, hi);
+          const u32x4 va = {l2[0], l2[1], h2v[0], h2v[1]};
+          oacc[d] = mfma32<DT>(va, pb, oacc[d]);
+        }
+      }
+    }
+  }
+
+  if (my_t < T) {
+    const float inv = 1.0f / l_run;
+    const size_t obase = ((size_t)b * T + my_t) * (size_t)(a.nh * HD) + h * HD;
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = d * 32 + g4 * 8 + h2 * 4;
+        store4_rt(a.o, obase + dd, a.out_dt, oacc[d][g4 * 4] * inv, oacc[d][g4 * 4 + 1] * inv,
+                  oacc[d][g4 * 4 + 2] * inv, oacc[d][g4 * 4 + 3] * inv);
+      }
+  }
+}
+
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   dim3 grid((a.T + PQ - 1) / PQ, a.nh, a.B);
   if (a.dt == DT_BF16) {
-    if (a.hd == 128) LL_LAUNCH((attn_prefill_kernel<DT_BF16, 128>), grid, dim3(256), 0, s, a);
+    if (a.hd == 128) LL_LAUNCH((attn_prefill_tr_kernel<DT_BF16>), grid, dim3(256), 0, s, a);
     else LL_LAUNCH((attn_prefill_kernel<DT_BF16, 64>), grid, dim3(256), 0, s, a);
   } else if (a.dt == DT_F16) {
-    if (a.hd == 128) LL_LAUNCH((attn_prefill_kernel<DT_F16, 128>), grid, dim3(256), 0, s, a);
+    if (a.hd == 128) LL_LAUNCH((attn_prefill_tr_kernel<DT_F16>), grid, dim3(256), 0, s, a);
     else LL_LAUNCH((attn_prefill_kernel<DT_F16, 64>), grid, dim3(256), 0, s, a);
   } else {
     return hipErrorInvalidValue;
