@@ -218,7 +218,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 // 64 banks once).  The DMA writes the swizzled layout by permuting each lane's
 // global address.
 template <int DT>
-__global__ __launch_bounds__(256) void attn_prefill_tr_kernel(AttnPrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_prefill_tr_kernel(AttnPrefillArgs a) {
   typedef typename Elt<DT>::T ET;
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   constexpr int HD = 128;
@@ -325,40 +326,49 @@ __global__ __launch_bounds__(256) void attn_prefill_tr_kernel(AttnPrefillArgs a)
         sacc[kb] = mfma32<DT>(kf, qf[s], sacc[kb]);
       }
     }
-    const bool need_mask = key0 + PKV - 1 > a.start_pos + wq0;
+    // Online softmax on unscaled scores; the scale folds into the exponent,
+    // p = 2^(s c - m c) with c = log2(e)/sqrt(hd).  The reference max m_run is
+    // only raised when a score exceeds it by more than 8 (log2 units), so the
+    // running sums are rarely rescaled and p stays <= 2^8.
+    if (key0 + PKV - 1 > a.start_pos + wq0) {  // diagonal tile: causal mask
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + (i >> 2) * 8 + h2 * 4 + (i & 3);
+          if (key > my_pos) sacc[kb][i] = -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float sv = sacc[kb][i] * qk_scale;
-        if (need_mask) {
-          const int key = key0 + kb * 32 + (i >> 2) * 8 + h2 * 4 + (i & 3);
-          if (key > my_pos) sv = -INFINITY;
-        }
-        sacc[kb][i] = sv;
-        mt = fmaxf(mt, sv);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * qk_scale;
+    const bool raise = mt > m_run + 8.f;  // also true on a lane's first visible key
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // 0 when m_run = -inf
+      const float m_new = raise ? mt : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      m_run = m_new;
+    }
+    // A lane with no visible key yet keeps m_run = -inf: its p are 0.
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(sacc[kb][i] - m_use);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], qk_scale, -m_use));
         sacc[kb][i] = p;
         rs += p;
       }
     rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < HD / 32; ++d)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+    l_run += rs;
 
     // O^T += V^T P^T.  MFMA (kb, hf) covers keys kb*32 + hf*16 + (e/4)*8 + h2*4 + e%4.
 #pragma unroll
