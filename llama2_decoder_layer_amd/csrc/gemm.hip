@@ -260,10 +260,106 @@ __global__ __launch_bounds__(256) void gemm_kernel(ProjArgs a) {
 template <int BM, int NW>
 struct DmaOcc { static constexpr int waves = (BM == 256 && NW == 4) ? 1 : 2; };
 
+// Tile geometry of the direct-to-LDS kernel.  Wave grid over (rows, tokens):
+// 2 x NW/2; SwiGLU 1 x NW (gate and up rows of a feature in the same wave).
+template <int EPI, int BM, int BN, int NW>
+struct DmaTile {
+  static constexpr bool SWI = (EPI == EPI_SWIGLU);
+  static constexpr int FM = SWI ? BM / 2 : BM;     // output features per tile
+  static constexpr int WN = SWI ? NW : NW / 2;     // waves along tokens
+  static constexpr int RB = SWI ? BM / 32 : BM / 64;
+  static constexpr int CB = BN / WN / 32;
+  static constexpr int ACC = RB * CB * 16;         // accumulators per lane
+};
+
+// Tile t -> first feature and first token: groups of GROUP_M weight panels,
+// token panels inner.
+__device__ __forceinline__ void dma_tile_origin(int t, int ntm, int ntn, int fm, int bn, int& f0,
+                                                int& n0) {
+  const int per_group = GROUP_M * ntn;
+  const int grp = t / per_group;
+  const int first_m = grp * GROUP_M;
+  const int gm = min(ntm - first_m, GROUP_M);
+  const int in_grp = t - grp * per_group;
+  f0 = (first_m + in_grp % gm) * fm;
+  n0 = (in_grp / gm) * bn;
+}
+
+// First row and token of each 32 x 32 accumulator block of this wave.
+template <int EPI, int BM, int BN, int NW>
+__device__ __forceinline__ void dma_wave_bases(int wave, int (&row_base)[DmaTile<EPI, BM, BN, NW>::RB],
+                                               int (&col_base)[DmaTile<EPI, BM, BN, NW>::CB]) {
+  typedef DmaTile<EPI, BM, BN, NW> G;
+  if constexpr (G::SWI) {
+#pragma unroll
+    for (int r = 0; r < G::RB; ++r) row_base[r] = r * 32;
+#pragma unroll
+    for (int c = 0; c < G::CB; ++c) col_base[c] = wave * (BN / G::WN) + c * 32;
+  } else {
+    const int wm = wave / G::WN, wn = wave % G::WN;
+#pragma unroll
+    for (int r = 0; r < G::RB; ++r) row_base[r] = wm * (BM / 2) + r * 32;
+#pragma unroll
+    for (int c = 0; c < G::CB; ++c) col_base[c] = wn * (BN / G::WN) + c * 32;
+  }
+}
+
+// Epilogue of one tile from a lane's accumulators (residual add, SwiGLU, or
+// RoPE + KV append).
+template <int DT, int EPI, int BM, int BN, int KVDT, int NW>
+__device__ __forceinline__ void dma_store_tile(const ProjArgs& a,
+                                               f32x16 (&acc)[DmaTile<EPI, BM, BN, NW>::RB]
+                                                            [DmaTile<EPI, BM, BN, NW>::CB],
+                                               int f0, int n0, int wave, int lane) {
+  typedef typename Elt<DT>::T T;
+  typedef DmaTile<EPI, BM, BN, NW> G;
+  int row_base[G::RB], col_base[G::CB];
+  dma_wave_bases<EPI, BM, BN, NW>(wave, row_base, col_base);
+  const int l32 = lane & 31, h2 = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < G::CB; ++c) {
+    const int m = n0 + col_base[c] + l32;
+    if (m >= a.M) continue;
+    const int mb = m / a.T, mt = m - mb * a.T, mpos = a.start_pos + mt;  // QKV only
+#pragma unroll
+    for (int r = 0; r < (G::SWI ? G::RB / 2 : G::RB); ++r) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int f = f0 + row_base[r] + g4 * 8 + h2 * 4;
+        if (f >= a.N) continue;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = acc[r][c][g4 * 4 + i];
+        if constexpr (EPI == EPI_RESID) {
+          const T* rp = reinterpret_cast<const T*>(a.resid) + (size_t)m * a.N + f;
+          float rv[4];
+          load4<DT>(rp, rv);
+          T* y = reinterpret_cast<T*>(a.y) + (size_t)m * a.N + f;
+          store4<DT>(y, rv[0] + v[0], rv[1] + v[1], rv[2] + v[2], rv[3] + v[3]);
+        } else if constexpr (G::SWI) {
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = silu(v[i]) * acc[r + G::RB / 2][c][g4 * 4 + i];
+          T* y = reinterpret_cast<T*>(a.y) + (size_t)m * a.N + f;
+          store4<DT>(y, o[0], o[1], o[2], o[3]);
+        } else {
+          gemm_qkv_store<KVDT>(a, mb, mt, mpos, f, v);
+        }
+      }
+    }
+  }
+}
+
+// Workgroups [0, full_tiles) each take a whole tile.  When the tiles do not
+// fill a whole number of rounds over the CUs, the remaining tiles are split
+// along K into ksplit parts, one workgroup each, so the last round is full;
+// those write float32 partials (accumulator quads of all threads in turn, so
+// the stores and loads coalesce) and gemm_split_reduce_kernel sums them and
+// applies the epilogue.
 template <int DT, int EPI, int BM, int BN, int KVDT, int NW>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(DmaOcc<BM, NW>::waves, DmaOcc<BM, NW>::waves)))
-void gemm_dma_kernel(ProjArgs a) {
+void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
   typedef typename Elt<DT>::T T;
   constexpr int BK = 32;
   constexpr int NST = 4;
@@ -272,13 +368,11 @@ void gemm_dma_kernel(ProjArgs a) {
   constexpr int AI = BM / RPI / NW;            // A instructions per wave per stage
   constexpr int BI = BN / RPI / NW;
   constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr bool SWI = (EPI == EPI_SWIGLU);
-  constexpr int FM = SWI ? BM / 2 : BM;
-  // Wave grid over (rows, tokens): 2 x NW/2; SwiGLU 1 x NW (gate and up rows
-  // of a feature in the same wave).
-  constexpr int WN = SWI ? NW : NW / 2;        // waves along tokens
-  constexpr int RB = SWI ? BM / 32 : BM / 64;
-  constexpr int CB = BN / WN / 32;
+  typedef DmaTile<EPI, BM, BN, NW> G;
+  constexpr bool SWI = G::SWI;
+  constexpr int FM = G::FM;
+  constexpr int RB = G::RB;
+  constexpr int CB = G::CB;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
 
@@ -287,18 +381,29 @@ void gemm_dma_kernel(ProjArgs a) {
   const int K = a.K;
   const int ntm = (a.N + FM - 1) / FM;
   const int ntn = (a.M + BN - 1) / BN;
-  const int nb = gridDim.x;
+  // Workgroup i runs on XCD i % 8: give each XCD a contiguous range of the
+  // whole tiles and, separately, of the split parts, so every XCD gets its
+  // share of both.
   int b2 = blockIdx.x;
-  if ((nb & 7) == 0) b2 = (b2 & 7) * (nb >> 3) + (b2 >> 3);
-  const int per_group = GROUP_M * ntn;
-  const int grp = b2 / per_group;
-  const int first_m = grp * GROUP_M;
-  const int gm = min(ntm - first_m, GROUP_M);
-  const int in_grp = b2 - grp * per_group;
-  const int tile_m = first_m + in_grp % gm;
-  const int tile_n = in_grp / gm;
-  const int f0 = tile_m * FM;
-  const int n0 = tile_n * BN;
+  {
+    const bool in_full = b2 < full_tiles;
+    const int lo = in_full ? 0 : full_tiles;
+    const int n = in_full ? full_tiles : gridDim.x - full_tiles;
+    const int i = b2 - lo;
+    if ((n & 7) == 0) b2 = lo + (i & 7) * (n >> 3) + (i >> 3);
+  }
+  // Whole tile, or one K part of a split tile.
+  const int nkt_all = K / BK;
+  int tile = b2, kt_begin = 0, kt_end = nkt_all, pidx = -1;
+  if (b2 >= full_tiles) {
+    pidx = b2 - full_tiles;
+    tile = full_tiles + pidx / ksplit;
+    const int per = (nkt_all + ksplit - 1) / ksplit;
+    kt_begin = min(nkt_all, (pidx % ksplit) * per);
+    kt_end = min(nkt_all, kt_begin + per);
+  }
+  int f0, n0;
+  dma_tile_origin(tile, ntm, ntn, FM, BN, f0, n0);
 
   // DMA sources: lane l fills row (l / 4) of its 16-row slab, physical chunk
   // l % 4, i.e. logical chunk (l % 4) ^ ((row >> 2) & 3).  Rows past N or M
@@ -329,7 +434,7 @@ void gemm_dma_kernel(ProjArgs a) {
   }
   auto issue = [&](int st, int kt) {
     uint8_t* base = lds + st * STAGE;
-    const int k = kt * BK;
+    const int k = (kt_begin + kt) * BK;
 #pragma unroll
     for (int i = 0; i < AI; ++i) dma16(asrc[i] + k, base + (wave * AI + i) * 1024);
 #pragma unroll
@@ -337,18 +442,7 @@ void gemm_dma_kernel(ProjArgs a) {
   };
 
   int row_base[RB], col_base[CB];
-  if constexpr (SWI) {
-#pragma unroll
-    for (int r = 0; r < RB; ++r) row_base[r] = r * 32;
-#pragma unroll
-    for (int c = 0; c < CB; ++c) col_base[c] = wave * (BN / WN) + c * 32;
-  } else {
-    const int wm = wave / WN, wn = wave % WN;
-#pragma unroll
-    for (int r = 0; r < RB; ++r) row_base[r] = wm * (BM / 2) + r * 32;
-#pragma unroll
-    for (int c = 0; c < CB; ++c) col_base[c] = wn * (BN / WN) + c * 32;
-  }
+  dma_wave_bases<EPI, BM, BN, NW>(wave, row_base, col_base);
   const int l32 = lane & 31, h2 = lane >> 5;
   int aoff[RB], boff[CB];  // byte offsets of this lane's fragment rows (chunk added per step)
 #pragma unroll
@@ -392,7 +486,7 @@ void gemm_dma_kernel(ProjArgs a) {
     else wait_vmcnt<0>();
   };
 
-  const int nkt = K / BK;
+  const int nkt = kt_end - kt_begin;
 #pragma unroll
   for (int st = 0; st < NST; ++st)
     if (st < nkt) issue(st, st);
@@ -439,45 +533,99 @@ void gemm_dma_kernel(ProjArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  if (pidx >= 0) {  // one K part of a split tile: float32 partials, [part][quad][thread]
+    f32x4* p = reinterpret_cast<f32x4*>(part) + (size_t)pidx * (G::ACC / 4) * (NW * 64) + tid;
 #pragma unroll
-  for (int c = 0; c < CB; ++c) {
-    const int m = n0 + col_base[c] + l32;
-    if (m >= a.M) continue;
-    const int mb = m / a.T, mt = m - mb * a.T, mpos = a.start_pos + mt;  // QKV only
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int r = 0; r < (SWI ? RB / 2 : RB); ++r) {
+      for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int f = f0 + row_base[r] + g4 * 8 + h2 * 4;
-        if (f >= a.N) continue;
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = acc[r][c][g4 * 4 + i];
-        if constexpr (EPI == EPI_RESID) {
-          const T* rp = reinterpret_cast<const T*>(a.resid) + (size_t)m * a.N + f;
-          float rv[4];
-          load4<DT>(rp, rv);
-          T* y = reinterpret_cast<T*>(a.y) + (size_t)m * a.N + f;
-          store4<DT>(y, rv[0] + v[0], rv[1] + v[1], rv[2] + v[2], rv[3] + v[3]);
-        } else if constexpr (SWI) {
-          float o[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = silu(v[i]) * acc[r + RB / 2][c][g4 * 4 + i];
-          T* y = reinterpret_cast<T*>(a.y) + (size_t)m * a.N + f;
-          store4<DT>(y, o[0], o[1], o[2], o[3]);
-        } else {
-          gemm_qkv_store<KVDT>(a, mb, mt, mpos, f, v);
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[r][c][4 * q], acc[r][c][4 * q + 1], acc[r][c][4 * q + 2],
+                           acc[r][c][4 * q + 3]};
+          p[(size_t)((r * CB + c) * 4 + q) * (NW * 64)] = v;
         }
-      }
-    }
+    return;
   }
+  dma_store_tile<DT, EPI, BM, BN, KVDT, NW>(a, acc, f0, n0, wave, lane);
 }
 
-// 256 x 256 tiles when they still give ~3 rounds of workgroups over the CUs.
-static bool use_big_tile(int epi, int N, int M) {
+// Sum of the K parts of each split tile, then the tile's epilogue.  Thread
+// layout and accumulator order as in gemm_dma_kernel; each tile's threads are
+// spread over NW/2 workgroups of two waves, so the reduction uses many CUs.
+constexpr int SPLIT_REDUCE_THREADS = 128;
+template <int DT, int EPI, int BM, int BN, int KVDT, int NW>
+__global__ __launch_bounds__(SPLIT_REDUCE_THREADS) void gemm_split_reduce_kernel(
+    ProjArgs a, const float* part, int full_tiles, int ksplit) {
+  typedef DmaTile<EPI, BM, BN, NW> G;
+  constexpr int PER_TILE = NW * 64 / SPLIT_REDUCE_THREADS;
+  const int tile_local = blockIdx.x / PER_TILE;
+  const int tid = (blockIdx.x - tile_local * PER_TILE) * SPLIT_REDUCE_THREADS + threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int tile = full_tiles + tile_local;
+  f32x16 acc[G::RB][G::CB];
+#pragma unroll
+  for (int r = 0; r < G::RB; ++r)
+#pragma unroll
+    for (int c = 0; c < G::CB; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
+  for (int sp = 0; sp < ksplit; ++sp) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(part) +
+                     (size_t)(tile_local * ksplit + sp) * (G::ACC / 4) * (NW * 64) + tid;
+#pragma unroll
+    for (int r = 0; r < G::RB; ++r)
+#pragma unroll
+      for (int c = 0; c < G::CB; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = p[(size_t)((r * G::CB + c) * 4 + q) * (NW * 64)];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][c][4 * q + i] += v[i];
+        }
+  }
+  const int ntm = (a.N + G::FM - 1) / G::FM;
+  const int ntn = (a.M + BN - 1) / BN;
+  int f0, n0;
+  dma_tile_origin(tile, ntm, ntn, G::FM, BN, f0, n0);
+  dma_store_tile<DT, EPI, BM, BN, KVDT, NW>(a, acc, f0, n0, wave, lane);
+}
+
+// Workgroups resident at once with 256 x 256 tiles (one per CU on gfx950's
+// 256 CUs): a "round".
+constexpr int GEMM_ROUND = 256;
+
+static long big_tiles(int epi, int N, int M) {
   const int fm = (epi == EPI_SWIGLU) ? 128 : 256;
-  const long tiles = (long)((N + fm - 1) / fm) * ((M + 255) / 256);
-  return tiles >= 3 * 256;
+  return (long)((N + fm - 1) / fm) * ((M + 255) / 256);
+}
+
+// Register-staged kernel: 256 x 256 tiles when they give ~3 rounds.
+static bool use_big_tile(int epi, int N, int M) { return big_tiles(epi, N, M) >= 3 * GEMM_ROUND; }
+
+// Direct-to-LDS kernel: 256 x 256 tiles from one full round on; a partly
+// filled last round is made full by splitting its tiles along K.
+struct DmaSplit {
+  int full, ksplit, grid;
+};
+static DmaSplit dma_split(long ntiles, int nkt) {
+  DmaSplit d{(int)ntiles, 1, (int)ntiles};
+  const long full = (ntiles / GEMM_ROUND) * GEMM_ROUND, rem = ntiles - full;
+  if (full == 0 || rem == 0) return d;
+  const int ks = (int)std::min<long>(std::min<long>(GEMM_ROUND / rem, 4), nkt);
+  if (ks < 2) return d;
+  d.full = (int)full;
+  d.ksplit = ks;
+  d.grid = (int)(full + rem * ks);
+  return d;
+}
+static bool dma_big(int epi, int N, int M) { return big_tiles(epi, N, M) >= GEMM_ROUND; }
+
+size_t gemm_partial_bytes(int epi, int N, int M, int K) {
+  if (K % 32 != 0 || !dma_big(epi, N, M)) return 0;
+  const DmaSplit d = dma_split(big_tiles(epi, N, M), K / 32);
+  // 512 threads x 128 accumulators (8 waves, 256 x 256 tile) per K part
+  return (size_t)(d.grid - d.full) * 512 * 128 * sizeof(float);
 }
 
 template <int DT, int EPI, int BM, int BN, int KVDT>
@@ -491,17 +639,28 @@ static hipError_t gemm_launch(const ProjArgs& a, hipStream_t s) {
 template <int DT, int EPI, int BM, int BN, int KVDT, int NW>
 static hipError_t gemm_dma_launch(const ProjArgs& a, hipStream_t s) {
   const int fm = (EPI == EPI_SWIGLU) ? BM / 2 : BM;
-  const int ntiles = ((a.N + fm - 1) / fm) * ((a.M + BN - 1) / BN);
-  LL_LAUNCH((gemm_dma_kernel<DT, EPI, BM, BN, KVDT, NW>), dim3(ntiles), dim3(NW * 64), 0, s, a);
+  const long ntiles = (long)((a.N + fm - 1) / fm) * ((a.M + BN - 1) / BN);
+  DmaSplit d{(int)ntiles, 1, (int)ntiles};
+  if (BM == 256) d = dma_split(ntiles, a.K / 32);
+  if (d.grid != d.full && !a.part) return hipErrorInvalidValue;
+  LL_LAUNCH((gemm_dma_kernel<DT, EPI, BM, BN, KVDT, NW>), dim3(d.grid), dim3(NW * 64), 0, s, a,
+            a.part, d.full, d.ksplit);
+  if (d.grid != d.full) {
+    static_assert(DmaTile<EPI, 256, 256, GEMM_BIG_WAVES>::ACC * GEMM_BIG_WAVES * 64 == 512 * 128,
+                  "partial size per K part");
+    LL_LAUNCH((gemm_split_reduce_kernel<DT, EPI, BM, BN, KVDT, NW>),
+              dim3(((int)ntiles - d.full) * (NW * 64 / SPLIT_REDUCE_THREADS)),
+              dim3(SPLIT_REDUCE_THREADS), 0, s, a, (const float*)a.part, d.full, d.ksplit);
+  }
   return hipGetLastError();
 }
 
 template <int DT, int EPI, int KVDT>
 static hipError_t gemm_epi(const ProjArgs& a, hipStream_t s) {
-  const bool big = use_big_tile(EPI, a.N, a.M);
   if (a.K % 32 == 0)
-    return big ? gemm_dma_launch<DT, EPI, 256, 256, KVDT, GEMM_BIG_WAVES>(a, s)
-               : gemm_dma_launch<DT, EPI, 128, 128, KVDT, 4>(a, s);
+    return dma_big(EPI, a.N, a.M) ? gemm_dma_launch<DT, EPI, 256, 256, KVDT, GEMM_BIG_WAVES>(a, s)
+                                  : gemm_dma_launch<DT, EPI, 128, 128, KVDT, 4>(a, s);
+  const bool big = use_big_tile(EPI, a.N, a.M);
   return big ? gemm_launch<DT, EPI, 256, 256, KVDT>(a, s) : gemm_launch<DT, EPI, 128, 128, KVDT>(a, s);
 }
 

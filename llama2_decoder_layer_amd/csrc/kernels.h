@@ -43,7 +43,11 @@ struct ProjArgs {
 // needs the M activation rows to fit the LDS stage: gemv_fits_lds(dt, M, K).
 hipError_t launch_gemv(int dt, int epi, const ProjArgs& a, hipStream_t s);
 bool gemv_fits_lds(int dt, int M, int K);
+// Prefill projection (M tokens): MFMA tiles with fused epilogues.  When the
+// last round of 256 x 256 tiles would leave CUs idle, its tiles are split
+// along K; the partials go to a.part, which must hold gemm_partial_bytes.
 hipError_t launch_gemm(int dt, int epi, const ProjArgs& a, hipStream_t s);
+size_t gemm_partial_bytes(int epi, int N, int M, int K);
 
 // Weight-streaming projection through LDS for 16-bit formats (K % 64 == 0,
 // N % 4 == 0, M <= 32, no fused norm); launch_gemv picks it when the row

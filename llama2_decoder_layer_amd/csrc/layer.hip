@@ -132,6 +132,14 @@ static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide) {
   if (wide) {
     L.u = take(bt * c->hidden * act);
     L.q16 = take(bt * qd * esize(c->kv_dtype));
+    // K-split partials of the prefill GEMMs.
+    const int H = c->hidden, I = c->intermediate, M = (int)bt;
+    const int qkv = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+    size_t pb = gemm_partial_bytes(EPI_QKV, qkv, M, H);
+    pb = std::max(pb, gemm_partial_bytes(EPI_RESID, H, M, (int)qd));
+    pb = std::max(pb, gemm_partial_bytes(EPI_SWIGLU, I, M, H));
+    pb = std::max(pb, gemm_partial_bytes(EPI_RESID, H, M, I));
+    L.part = take(pb);
   } else {
     // Token-skinny plans process at most 32 tokens at a time.
     const int64_t g = std::min<int64_t>(bt, 32);
@@ -309,7 +317,9 @@ static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void
   LL_TRY(launch_rmsnorm(dt, x, w->attn_norm, u, M, H, c->eps, s));
   timer_after(KID_RMSNORM, s);
 
+  float* part = (float*)(ws + L.part);
   ProjArgs p = base_args(c);
+  p.part = part;
   p.w[0] = w->w_q; p.w[1] = w->w_k; p.w[2] = w->w_v;
   p.seg1 = qd; p.seg2 = qd + kd;
   p.N = qd + 2 * kd; p.K = H; p.M = M; p.x = u;
@@ -328,6 +338,7 @@ static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void
   timer_after(KID_ATTN_PREFILL, s);
 
   ProjArgs po = base_args(c);
+  po.part = part;
   po.w[0] = w->w_o; po.seg1 = po.seg2 = H;
   po.N = H; po.K = qd; po.M = M; po.x = ws + L.o; po.resid = x; po.y = ws + L.h1;
   timer_before(KID_GEMM_O, s);
@@ -339,6 +350,7 @@ static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void
   timer_after(KID_RMSNORM, s);
 
   ProjArgs pg = base_args(c);
+  pg.part = part;
   pg.w[0] = w->w_gate; pg.w[1] = w->w_up;
   pg.N = I; pg.K = H; pg.M = M; pg.x = u; pg.y = ws + L.a;
   timer_before(KID_GEMM_GATEUP, s);
@@ -346,6 +358,7 @@ static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void
   timer_after(KID_GEMM_GATEUP, s);
 
   ProjArgs pd = base_args(c);
+  pd.part = part;
   pd.w[0] = w->w_down; pd.seg1 = pd.seg2 = H;
   pd.N = H; pd.K = I; pd.M = M; pd.x = ws + L.a; pd.resid = ws + L.h1; pd.y = y;
   timer_before(KID_GEMM_DOWN, s);
