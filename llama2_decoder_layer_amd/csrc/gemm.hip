@@ -261,14 +261,17 @@ template <int BM, int NW>
 struct DmaOcc { static constexpr int waves = (BM == 256 && NW == 4) ? 1 : 2; };
 
 // Tile geometry of the direct-to-LDS kernel.  Wave grid over (rows, tokens):
-// 2 x NW/2; SwiGLU 1 x NW (gate and up rows of a feature in the same wave).
+// 2 x NW/2, each wave BM/2 rows x 2 BN/NW tokens.  With SwiGLU the tile's
+// rows are FM gate rows then the FM matching up rows, and wave half wm takes
+// gate rows [wm FM/2, (wm+1) FM/2) with the up rows of the same features, so
+// gate and up of a feature meet in one lane.
 template <int EPI, int BM, int BN, int NW>
 struct DmaTile {
   static constexpr bool SWI = (EPI == EPI_SWIGLU);
   static constexpr int FM = SWI ? BM / 2 : BM;     // output features per tile
-  static constexpr int WN = SWI ? NW : NW / 2;     // waves along tokens
-  static constexpr int RB = SWI ? BM / 32 : BM / 64;
-  static constexpr int CB = BN / WN / 32;
+  static constexpr int WN = NW / 2;                // waves along tokens
+  static constexpr int RB = BM / 64;               // 32-row blocks per wave
+  static constexpr int CB = BN / WN / 32;          // 32-token blocks per wave
   static constexpr int ACC = RB * CB * 16;         // accumulators per lane
 };
 
@@ -290,18 +293,18 @@ template <int EPI, int BM, int BN, int NW>
 __device__ __forceinline__ void dma_wave_bases(int wave, int (&row_base)[DmaTile<EPI, BM, BN, NW>::RB],
                                                int (&col_base)[DmaTile<EPI, BM, BN, NW>::CB]) {
   typedef DmaTile<EPI, BM, BN, NW> G;
+  const int wm = wave / G::WN, wn = wave % G::WN;
   if constexpr (G::SWI) {
+    // blocks [0, RB/2): gate rows; [RB/2, RB): the up rows of the same features
 #pragma unroll
-    for (int r = 0; r < G::RB; ++r) row_base[r] = r * 32;
-#pragma unroll
-    for (int c = 0; c < G::CB; ++c) col_base[c] = wave * (BN / G::WN) + c * 32;
+    for (int r = 0; r < G::RB; ++r)
+      row_base[r] = (r < G::RB / 2 ? 0 : G::FM) + wm * (G::FM / 2) + (r % (G::RB / 2)) * 32;
   } else {
-    const int wm = wave / G::WN, wn = wave % G::WN;
 #pragma unroll
     for (int r = 0; r < G::RB; ++r) row_base[r] = wm * (BM / 2) + r * 32;
-#pragma unroll
-    for (int c = 0; c < G::CB; ++c) col_base[c] = wn * (BN / G::WN) + c * 32;
   }
+#pragma unroll
+  for (int c = 0; c < G::CB; ++c) col_base[c] = wn * (BN / G::WN) + c * 32;
 }
 
 // Epilogue of one tile from a lane's accumulators (residual add, SwiGLU, or
