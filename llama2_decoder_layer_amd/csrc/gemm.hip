@@ -245,13 +245,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(ProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant (K % 32 == 0).  Operands move global -> LDS with
-// global_load_lds_dwordx4 (lane l of a wave writes bytes [16 l, 16 l + 16) of
-// the LDS destination), so no registers stage them and no ds_write is issued;
-// the swizzled LDS layout comes from permuting each lane's global address.
-// 32-k stages, NST of them in LDS, loads NST-1 stages ahead of the multiply.
-// A 32-k row slice is 64 bytes, four rows per 256-byte bank sweep: chunk c of
-// row r is stored at chunk c ^ ((r >> 2) & 3).
+// Direct-to-LDS variant (K % 32 == 0; K % 64 == 0 for 256 x 256 tiles).
+// Operands move global -> LDS with global_load_lds_dwordx4 (lane l of a wave
+// writes bytes [16 l, 16 l + 16) of the LDS destination), so no registers
+// stage them and no ds_write is issued; the swizzled LDS layout comes from
+// permuting each lane's global address.  BK-k stages, NST of them in LDS,
+// loads NST-1 stages ahead of the multiply.  A row slice is 2 BK bytes, and
+// the rows sharing a 256-byte bank sweep get distinct chunk orders: chunk c
+// of row r is stored at c ^ ((r / rows_per_sweep) % chunks_per_row).
 // ---------------------------------------------------------------------------
 // Occupancy target per SIMD: 4 waves on a 256 x 256 tile hold 256 accumulator
 // registers each (one wave per SIMD); 8 waves hold 128 (two per SIMD, so one
@@ -353,6 +354,25 @@ __device__ __forceinline__ void dma_store_tile(const ProjArgs& a,
   }
 }
 
+// Pipeline: k per stage and stages in LDS.  The 256 x 256 tile takes 64-k
+// stages (half the barriers per MFMA of 32-k stages), two of them (128 KB).
+#ifndef GEMM_BIG_BK
+#define GEMM_BIG_BK 64
+#endif
+template <int BM>
+struct DmaPipe {
+  static constexpr int BK = (BM == 256) ? GEMM_BIG_BK : 32;
+  static constexpr int NST = (BK == 64) ? 2 : 4;
+};
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Workgroups [0, full_tiles) each take a whole tile.  When the tiles do not
 // fill a whole number of rounds over the CUs, the remaining tiles are split
 // along K into ksplit parts, one workgroup each, so the last round is full;
@@ -364,10 +384,14 @@ __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(DmaOcc<BM, NW>::waves, DmaOcc<BM, NW>::waves)))
 void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
   typedef typename Elt<DT>::T T;
-  constexpr int BK = 32;
-  constexpr int NST = 4;
-  constexpr int ROWB = BK * 2;                 // 64 bytes per row slice
-  constexpr int RPI = 16;                      // rows per 1 KB wave instruction
+  constexpr int BK = DmaPipe<BM>::BK;
+  constexpr int NST = DmaPipe<BM>::NST;
+  constexpr int KS = BK / 16;                  // 16-k MFMA steps per stage
+  constexpr int ROWB = BK * 2;                 // bytes per row slice (64 or 128)
+  constexpr int LPR = ROWB / 16;               // lanes per row in a DMA instruction
+  constexpr int RPI = 64 / LPR;                // rows per 1 KB wave instruction
+  constexpr int RPS = 256 / ROWB;              // rows per 256-byte bank sweep
+  constexpr int CPR = ROWB / 16;               // 16-byte chunks per row slice
   constexpr int AI = BM / RPI / NW;            // A instructions per wave per stage
   constexpr int BI = BN / RPI / NW;
   constexpr int STAGE = (BM + BN) * ROWB;
@@ -408,16 +432,17 @@ void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
   int f0, n0;
   dma_tile_origin(tile, ntm, ntn, FM, BN, f0, n0);
 
-  // DMA sources: lane l fills row (l / 4) of its 16-row slab, physical chunk
-  // l % 4, i.e. logical chunk (l % 4) ^ ((row >> 2) & 3).  Rows past N or M
+  // DMA sources: lane l fills row l / LPR of its RPI-row slab, physical chunk
+  // l % LPR, i.e. logical chunk (l % LPR) ^ ((row / RPS) % CPR): the rows that
+  // share a 256-byte bank sweep get distinct chunk orders.  Rows past N or M
   // read row 0 (their results are never stored).
-  const int rr = lane >> 2, pc = lane & 3;
+  const int rr = lane / LPR, pc = lane % LPR;
   const T* asrc[AI];
   const T* bsrc[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int r = (wave * AI + i) * RPI + rr;
-    const int c = pc ^ ((r >> 2) & 3);
+    const int c = pc ^ ((r / RPS) % CPR);
     const T* row;
     if constexpr (SWI) {
       const int f = f0 + (r % FM);
@@ -431,7 +456,7 @@ void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
     const int r = (wave * BI + i) * RPI + rr;
-    const int c = pc ^ ((r >> 2) & 3);
+    const int c = pc ^ ((r / RPS) % CPR);
     const int m = n0 + r;
     bsrc[i] = reinterpret_cast<const T*>(a.x) + (size_t)(m < a.M ? m : 0) * K + c * 8;
   }
@@ -452,7 +477,8 @@ void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
   for (int r = 0; r < RB; ++r) aoff[r] = (row_base[r] + l32) * ROWB;
 #pragma unroll
   for (int c = 0; c < CB; ++c) boff[c] = BM * ROWB + (col_base[c] + l32) * ROWB;
-  const int swz_a = ((l32 >> 2) & 3);  // row_base is a multiple of 32: (row >> 2) & 3 == (l32 >> 2) & 3
+  // row_base is a multiple of 32, so (row / RPS) % CPR == (l32 / RPS) % CPR.
+  const int swz_a = (l32 / RPS) % CPR;
 
   f32x16 acc[RB][CB];
 #pragma unroll
@@ -462,23 +488,17 @@ void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
 
-  // Fragments of the two 16-k steps of a stage: X = step 0, Y = step 1.
-  u32x4 xa[RB], xb[CB], ya[RB], yb[CB];
-  auto read_x = [&](int st) {
+  // Two fragment sets alternate over the 16-k steps: the next step's
+  // fragments are read while the current step multiplies.
+  u32x4 fa[2][RB], fb[2][CB];
+  auto read_set = [&](auto set, int st, int ks) {
+    constexpr int S = decltype(set)::value;
     const uint8_t* base = lds + st * STAGE;
-    const int chb = ((0 + h2) ^ swz_a) * 16;
+    const int chb = ((2 * ks + h2) ^ swz_a) * 16;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) xa[r] = ld16(base + aoff[r] + chb);
+    for (int r = 0; r < RB; ++r) fa[S][r] = ld16(base + aoff[r] + chb);
 #pragma unroll
-    for (int c = 0; c < CB; ++c) xb[c] = ld16(base + boff[c] + chb);
-  };
-  auto read_y = [&](int st) {
-    const uint8_t* base = lds + st * STAGE;
-    const int chb = ((2 + h2) ^ swz_a) * 16;
-#pragma unroll
-    for (int r = 0; r < RB; ++r) ya[r] = ld16(base + aoff[r] + chb);
-#pragma unroll
-    for (int c = 0; c < CB; ++c) yb[c] = ld16(base + boff[c] + chb);
+    for (int c = 0; c < CB; ++c) fb[S][c] = ld16(base + boff[c] + chb);
   };
   // Wait until this wave's DMA of a stage has landed: at most the loads of the
   // `newer` stages issued after it may still be outstanding.
@@ -495,44 +515,45 @@ void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
     if (st < nkt) issue(st, st);
   wait_stage(min(NST, nkt) - 1);
   __builtin_amdgcn_s_barrier();
-  read_x(0);
+  read_set(ic<0>{}, 0, 0);
 
-  // Per stage kt: read step 1 while step 0 multiplies; then (all of stage kt
-  // read, stage kt+1 landed everywhere) refill stage kt's buffer with stage
-  // kt+NST and read stage kt+1's step 0 while step 1 multiplies.  Barriers are
-  // bare s_barrier: the waits that make them safe are explicit.  The
-  // sched_barriers pin this order (the scheduler would otherwise sink each
-  // fragment read next to its first use).
+  // Per 16-k step: the first half of its MFMAs, then the reads of the next
+  // step, then the second half.  After the first half of a stage's last step
+  // (all of the stage read, the next stage landed everywhere) comes the one
+  // barrier of the stage; then the buffer just finished is refilled with stage
+  // kt+NST and the next stage's first step is read.  Barriers are bare
+  // s_barrier: the waits that make them safe are explicit.  The sched_barriers
+  // pin this order (the scheduler would otherwise sink each fragment read next
+  // to its first use).
   for (int kt = 0; kt < nkt; ++kt) {
     const int st = kt % NST;
-    // First half of step 0's MFMAs (its fragments were read a step earlier),
-    // then the reads of step 1, then the rest of step 0.
-    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, KS>([&](auto KSI) {
+      constexpr int ks = decltype(KSI)::value;
+      constexpr int S = ks & 1;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < RB / 2; ++r)
+      for (int r = 0; r < RB / 2; ++r)
 #pragma unroll
-      for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(xa[r], xb[c], acc[r][c]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_y(st);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(fa[S][r], fb[S][c], acc[r][c]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ks + 1 < KS) {
+        read_set(ic<S ^ 1>{}, st, ks + 1);
+      } else {
+        // Unconditional (the last stage reads a valid buffer it never uses): a
+        // branch here makes the wait-count pass wait for these reads before
+        // the MFMAs below.
+        wait_lgkmcnt0();
+        wait_stage(max(min(kt + NST, nkt) - 1 - (kt + 1), 0));
+        __builtin_amdgcn_s_barrier();
+        if (kt + NST < nkt) issue(st, kt + NST);
+        read_set(ic<S ^ 1>{}, (kt + 1) % NST, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = RB / 2; r < RB; ++r)
+      for (int r = RB / 2; r < RB; ++r)
 #pragma unroll
-      for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(xa[r], xb[c], acc[r][c]);
-    __builtin_amdgcn_sched_barrier(0);
-    // Unconditional (the last stage reads a valid buffer it never uses): a
-    // branch here makes the wait-count pass wait for these reads before the
-    // step-1 MFMAs below.
-    wait_lgkmcnt0();
-    wait_stage(max(min(kt + NST, nkt) - 1 - (kt + 1), 0));
-    __builtin_amdgcn_s_barrier();
-    if (kt + NST < nkt) issue(st, kt + NST);
-    read_x((kt + 1) % NST);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(ya[r], yb[c], acc[r][c]);
+        for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(fa[S][r], fb[S][c], acc[r][c]);
+    });
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -622,11 +643,13 @@ static DmaSplit dma_split(long ntiles, int nkt) {
   d.grid = (int)(full + rem * ks);
   return d;
 }
-static bool dma_big(int epi, int N, int M) { return big_tiles(epi, N, M) >= GEMM_ROUND; }
+static bool dma_big(int epi, int N, int M, int K) {
+  return K % DmaPipe<256>::BK == 0 && big_tiles(epi, N, M) >= GEMM_ROUND;
+}
 
 size_t gemm_partial_bytes(int epi, int N, int M, int K) {
-  if (K % 32 != 0 || !dma_big(epi, N, M)) return 0;
-  const DmaSplit d = dma_split(big_tiles(epi, N, M), K / 32);
+  if (K % 32 != 0 || !dma_big(epi, N, M, K)) return 0;
+  const DmaSplit d = dma_split(big_tiles(epi, N, M), K / DmaPipe<256>::BK);
   // 512 threads x 128 accumulators (8 waves, 256 x 256 tile) per K part
   return (size_t)(d.grid - d.full) * 512 * 128 * sizeof(float);
 }
@@ -644,7 +667,7 @@ static hipError_t gemm_dma_launch(const ProjArgs& a, hipStream_t s) {
   const int fm = (EPI == EPI_SWIGLU) ? BM / 2 : BM;
   const long ntiles = (long)((a.N + fm - 1) / fm) * ((a.M + BN - 1) / BN);
   DmaSplit d{(int)ntiles, 1, (int)ntiles};
-  if (BM == 256) d = dma_split(ntiles, a.K / 32);
+  if (BM == 256) d = dma_split(ntiles, a.K / DmaPipe<BM>::BK);
   if (d.grid != d.full && !a.part) return hipErrorInvalidValue;
   LL_LAUNCH((gemm_dma_kernel<DT, EPI, BM, BN, KVDT, NW>), dim3(d.grid), dim3(NW * 64), 0, s, a,
             a.part, d.full, d.ksplit);
@@ -661,7 +684,7 @@ static hipError_t gemm_dma_launch(const ProjArgs& a, hipStream_t s) {
 template <int DT, int EPI, int KVDT>
 static hipError_t gemm_epi(const ProjArgs& a, hipStream_t s) {
   if (a.K % 32 == 0)
-    return dma_big(EPI, a.N, a.M) ? gemm_dma_launch<DT, EPI, 256, 256, KVDT, GEMM_BIG_WAVES>(a, s)
+    return dma_big(EPI, a.N, a.M, a.K) ? gemm_dma_launch<DT, EPI, 256, 256, KVDT, GEMM_BIG_WAVES>(a, s)
                                   : gemm_dma_launch<DT, EPI, 128, 128, KVDT, 4>(a, s);
   const bool big = use_big_tile(EPI, a.N, a.M);
   return big ? gemm_launch<DT, EPI, 256, 256, KVDT>(a, s) : gemm_launch<DT, EPI, 128, 128, KVDT>(a, s);
