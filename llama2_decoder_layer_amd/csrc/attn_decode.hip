@@ -66,14 +66,14 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnDecodeArgs a) {
     const int key = k_lo + slot + i * KPI;
     const bool ok = key < k_hi;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[i][c] = ok ? ld16(kp + (size_t)key * HD + c * (8 / NC)) : zero;
+    for (int c = 0; c < NC; ++c) kr[i][c] = ok ? ld16_stream(kp + (size_t)key * HD + c * (8 / NC)) : zero;
   }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int key = k_lo + slot + i * KPI;
     const bool ok = key < k_hi;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[i][c] = ok ? ld16(vp + (size_t)key * HD + c * (8 / NC)) : zero;
+    for (int c = 0; c < NC; ++c) vr[i][c] = ok ? ld16_stream(vp + (size_t)key * HD + c * (8 / NC)) : zero;
   }
 
   float qf[GC][8];
@@ -240,7 +240,7 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
     for (int t = 0; t < TW; ++t) {
       const uint32_t key = (uint32_t)min(kb + 16 * t + r16, k_hi - 1);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) kr[t][s] = ld16(kp + (key * HD + 32 * s + ko));
+      for (int s = 0; s < NS; ++s) kr[t][s] = ld16_stream(kp + (key * HD + 32 * s + ko));
     }
   };
   auto load_v = [&](int it) {
@@ -248,7 +248,7 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const uint32_t key = (uint32_t)min(kb + vkey + KG * i, k_hi - 1);
-      vr[i] = ld16(vp + (key * HD + vo));
+      vr[i] = ld16_stream(vp + (key * HD + vo));
     }
   };
   load_k(0);

@@ -63,6 +63,11 @@ template <> struct Elt<DT_F16> {
 // 16-byte chunks <-> fp32 lanes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Streaming load (non-temporal hint) for data read once per call: weights in
+// decode, KV-cache rows.  Measured 2-8% faster than plain loads there.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Unpack a chunk of PER16 elements to floats (f[0..PER16)).
@@ -187,6 +192,10 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
+}
+// Same with the non-temporal cache policy (streamed data read once).
+__device__ __forceinline__ void dma16_stream(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 2);
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256) void gemv_row_kernel(ProjArgs a) {
 #pragma unroll
       for (int n = 0; n < NA; ++n)
 #pragma unroll
-        for (int r = 0; r < R; ++r) wv[u][n][r] = (k < K) ? ld16(wp[n][r] + k) : zero;
+        for (int r = 0; r < R; ++r) wv[u][n][r] = (k < K) ? ld16_stream(wp[n][r] + k) : zero;
     }
   };
   // Weight loads start before the activations are staged.

@@ -119,7 +119,10 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
     uint8_t* base = lds + st * SK_STAGE;
     const int k = kt * SK_BK;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) dma16(src[j] + k, base + (wave + 4 * j) * 1024);
+    for (int j = 0; j < 3; ++j) {
+      if (j < 2) dma16_stream(src[j] + k, base + (wave + 4 * j) * 1024);  // weights
+      else dma16(src[j] + k, base + (wave + 4 * j) * 1024);               // activations
+    }
   };
   // This wave's part of a stage has landed once at most `newer` later stages
   // (3 loads each) are outstanding.
