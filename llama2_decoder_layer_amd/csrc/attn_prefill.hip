@@ -20,6 +20,9 @@ namespace ll {
 constexpr int PQ = 128;   // queries per workgroup
 constexpr int PKV = 64;   // keys per tile
 constexpr int VT_STRIDE = PKV + 4;  // padded row of the transposed V tile (elements)
+// K/V tile stages in LDS (head_dim 128 kernel).  Two keep two workgroups per
+// CU; three or four (one workgroup per CU) measured 1.6-1.8x slower.
+constexpr int PF_STAGES = 2;
 
 template <int DT, int HD>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
@@ -228,7 +231,7 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
   constexpr int STAGE_B = 2 * TILE_B;            // K then V
   // One LDS object (a second one gives the accesses alias scopes, and the
   // wait-count pass then waits for every outstanding DMA before each read).
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[PF_STAGES * STAGE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -299,16 +302,24 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
     return row * ROWB + (((col >> 3) ^ (4 * (ii >> 2))) << 4) + ((col >> 2) & 1) * 8;
   };
 
-  issue(0, 0);
+  // Tiles t+1 .. t+PF_STAGES-1 load while tile t is used (8 DMA loads per
+  // wave and tile).
+#pragma unroll
+  for (int t = 0; t < PF_STAGES - 1; ++t)
+    if (t < ntiles) issue(t, t * PKV);
   for (int tile = 0; tile < ntiles; ++tile) {
     const int key0 = tile * PKV;
-    wait_vmcnt<0>();
+    const int newer = min(ntiles - 1, tile + PF_STAGES - 2) - tile;
+    if (newer >= 2) wait_vmcnt<16>();
+    else if (newer == 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();  // tile landed everywhere; the other buffer is free
+    __builtin_amdgcn_s_barrier();  // tile landed everywhere; tile-1's buffer is free
     __builtin_amdgcn_sched_barrier(0);
-    if (tile + 1 < ntiles) issue((tile + 1) & 1, key0 + PKV);
+    if (tile + PF_STAGES - 1 < ntiles)
+      issue((tile + PF_STAGES - 1) % PF_STAGES, (tile + PF_STAGES - 1) * PKV);
     if (key0 > w_last_pos) continue;  // every key of this tile is in this wave's future
-    const uint8_t* kt = lds + (tile & 1) * STAGE_B;
+    const uint8_t* kt = lds + (tile % PF_STAGES) * STAGE_B;
     const uint8_t* vt = kt + TILE_B;
 
     f32x16 sacc[2];
