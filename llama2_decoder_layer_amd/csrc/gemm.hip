@@ -618,6 +618,9 @@ __global__ __launch_bounds__(SPLIT_REDUCE_THREADS) void gemm_split_reduce_kernel
 // Workgroups resident at once with 256 x 256 tiles (one per CU on gfx950's
 // 256 CUs): a "round".
 constexpr int GEMM_ROUND = 256;
+#ifndef GEMM_BIG_MIN_FRAC
+#define GEMM_BIG_MIN_FRAC 4
+#endif
 
 static long big_tiles(int epi, int N, int M) {
   const int fm = (epi == EPI_SWIGLU) ? 128 : 256;
@@ -635,16 +638,19 @@ struct DmaSplit {
 static DmaSplit dma_split(long ntiles, int nkt) {
   DmaSplit d{(int)ntiles, 1, (int)ntiles};
   const long full = (ntiles / GEMM_ROUND) * GEMM_ROUND, rem = ntiles - full;
-  if (full == 0 || rem == 0) return d;
-  const int ks = (int)std::min<long>(std::min<long>(GEMM_ROUND / rem, 4), nkt);
+  if (rem == 0) return d;
+  // Less than one round: split every tile until the parts fill a round.
+  const int ks = full == 0 ? (int)std::min<long>(std::min<long>((GEMM_ROUND + rem - 1) / rem, 4), nkt)
+                           : (int)std::min<long>(std::min<long>(GEMM_ROUND / rem, 4), nkt);
   if (ks < 2) return d;
   d.full = (int)full;
   d.ksplit = ks;
   d.grid = (int)(full + rem * ks);
   return d;
 }
+// 256 x 256 tiles from a quarter round on (smaller launches split along K).
 static bool dma_big(int epi, int N, int M, int K) {
-  return K % DmaPipe<256>::BK == 0 && big_tiles(epi, N, M) >= GEMM_ROUND;
+  return K % DmaPipe<256>::BK == 0 && big_tiles(epi, N, M) >= GEMM_ROUND / GEMM_BIG_MIN_FRAC;
 }
 
 size_t gemm_partial_bytes(int epi, int N, int M, int K) {
