@@ -162,6 +162,16 @@ def test_bf16_prefill_wide_hd128_gqa_offset():
                      50, 400, 121)
 
 
+def test_bf16_prefill_split_k_tiles():
+    # 2 sequences x 1280 tokens at hidden 1024: QKV (3072 features, 10 x 12
+    # tiles of 256) and gate/up (2816 features) fall below one round of
+    # 256 x 256 tiles and are split along K; O and down take 128 x 128 tiles.
+    # Rows sampled across token tiles, every appended K/V entry checked.
+    rows = np.array([0, 1, 255, 256, 700, 1023, 1024, 1279])
+    run_prefill_case("bf16-prefill-split-k", S.Shape(1024, 8, 8, 128, 2816), "bf16", "bf16", 2,
+                     1280, 0, 1280, 131, out_rows=rows)
+
+
 def test_bf16_prefill_wide_f16_cache_mqa():
     run_prefill_case("bf16-prefill-f16kv", S.Shape(256, 4, 1, 64, 512), "bf16", "f16", 1, 130, 3,
                      140, 122)
