@@ -179,34 +179,47 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnDecodeArgs a) {
   }
 }
 
-// GQA variant for 16-bit caches with GC = 4 or 8 query heads per workgroup.
-// The scores of a 16-key tile come from v_mfma_f32_16x16x32 with K in the A
-// layout (lane: key r16, dims 32s + 8(l/16) of slice s, loaded straight from
-// the cache as 64-byte row pieces) and the group's queries in the B layout
-// (head r16; columns past GC are zero), so no cross-lane dot-product
-// reductions are needed.  P V runs on the VALU with each lane holding 8 dims
-// of its V rows (V would need a transpose to be an MFMA operand); P and the
-// rescale factors reach those lanes through a per-wave LDS area.
+// GQA variant for 16-bit caches with GC = 4 or 8 query heads per workgroup;
+// both products run on the matrix cores.
+//
+// Scores of a 16-key tile: v_mfma_f32_16x16x32 with K in the A layout (lane:
+// key r16, dims 32s + 8(l/16) of slice s) and the group's queries in the B
+// layout (head r16; columns past GC are zero).  The result leaves lane l with
+// head l%16 and keys 4(l/16) + 0..3, which is exactly the A layout of a
+// 16x16x16 MFMA with P as A (heads x keys), so P V needs no data movement
+// for P.  V (keys x dims) is the B operand, read with ds_read_b64_tr_b16,
+// which hands lane l the 4 keys of k-group l/16 for dim l%16.
 //
 // Each wave streams its own keys, 16 per iteration (keys k_lo + 64 it +
 // 16 wave + [0, 16)), with an online softmax, so the waves never wait for each
 // other until the end, where their (max, sum, acc) are combined in LDS.  The
-// next iteration's K rows are requested right after the scores consume the
-// current ones, and its V rows right after P V.  Queries are rounded to the
-// cache format for the MFMA.  Output: the same partials as attn_split_kernel,
-// one split per CH = 64 NIT keys.
+// K and V rows of an iteration go to the wave's own LDS ring by
+// global_load_lds, two iterations ahead, with explicit wait counts: every
+// vector-memory load in the loop is such a DMA.  (Register loads in flight
+// next to LDS loads make the compiler wait for all of them before any use.)
+// The 16-byte chunks of a K row are XOR-swizzled by row & 15 (fragment reads
+// of 16 rows hit 16 bank groups) and those of a V row by 2 (row & 3) (the 16
+// lanes of a transposed read hit 16 bank pairs); the swizzle is applied on
+// the global side, since the DMA writes each instruction's 1 KB linearly.
+// Queries and P are rounded to the cache format for the MFMAs.  Output: the
+// same partials as attn_split_kernel, one split per CH = 64 NIT keys.
 template <int KVDT, int HD, int GC, int NIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_gqa_kernel(AttnDecodeArgs a) {
   typedef typename Elt<KVDT>::T T;
-  constexpr int NS = HD / 32;   // 32-dim slices: MFMAs per 16-key tile
-  constexpr int TW = 1;         // 16-key tiles per wave and iteration
-  constexpr int KW = 16 * TW;   // keys per wave and iteration
-  constexpr int WI = 4 * KW;    // keys per workgroup and iteration
-  constexpr int CH = WI * NIT;  // keys per workgroup
-  constexpr int DGN = HD / 8;   // 8-dim groups of a row
-  constexpr int KG = 64 / DGN;  // V rows per wave load instruction
-  constexpr int KPL = KW / KG;  // V rows per lane and iteration
+  constexpr int NS = HD / 32;         // 32-dim slices: score MFMAs per tile
+  constexpr int ND = HD / 16;         // 16-dim output tiles: P V MFMAs per tile
+  constexpr int KW = 16;              // keys per wave and iteration
+  constexpr int WI = 4 * KW;          // keys per workgroup and iteration
+  constexpr int CH = WI * NIT;        // keys per workgroup
+  constexpr int ROW = HD * 2;         // bytes of one K or V row
+  constexpr int TILE = KW * ROW;      // one wave's K (or V) rows of one iteration
+  constexpr int TI = TILE / 1024;     // DMA instructions per tile
+  constexpr int RPI = 1024 / ROW;     // rows per DMA instruction
+  constexpr int CPR = ROW / 16;       // 16-byte chunks per row
+  constexpr int WAVE_LDS = 4 * TILE;  // K and V rings of one wave
+  constexpr int RING = 4 * WAVE_LDS;
+  static_assert(4 * GC * HD * 4 <= RING, "the wave sums reuse the rings");
   const int split = blockIdx.x;
   const int g = a.nh / a.nkv;
   const int per_kv = g / GC;
@@ -220,179 +233,184 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
   if (k_lo >= k_hi) return;  // past this query's context: not counted, not merged
   const int nit = (k_hi - k_lo + WI - 1) / WI;
 
+  // One LDS object (a second one would make the compiler wait for every
+  // outstanding load before each LDS read): per-wave K and V rings, then
+  // per-wave rescale factors, maxima and sums.  The cross-wave sums reuse the
+  // rings.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + 3 * 4 * 16 * 4];
+  float* s_alpha = reinterpret_cast<float*>(lds + RING);  // [4][16]
+  float* s_m = s_alpha + 64;                              // [4][16]
+  float* s_l = s_m + 64;                                  // [4][16]
+  float* s_acc = reinterpret_cast<float*>(lds);           // [4][GC][HD] after the loop
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int vdg = lane % DGN, vkey = lane / DGN;
+  uint8_t* kring = lds + wave * WAVE_LDS;  // [2][TILE]
+  uint8_t* vring = kring + 2 * TILE;       // [2][TILE]
   const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD;
   const T* kp = reinterpret_cast<const T*>(a.kc) + head_off;
   const T* vp = reinterpret_cast<const T*>(a.vc) + head_off;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  // Offsets within one head's rows fit 32 bits: loads take a uniform base
-  // plus a 32-bit lane offset.
-  const uint32_t ko = 8u * g4, vo = 8u * vdg;  // element offsets within a row
 
-  // Rows past the chunk's end read the last valid row (finite values whose
-  // scores are masked and whose P is zero), so the loads need no branches.
-  u32x4 kr[TW][NS], vr[KPL];
-  auto load_k = [&](int it) {
-    const int kb = k_lo + WI * it + KW * wave;
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      const uint32_t key = (uint32_t)min(kb + 16 * t + r16, k_hi - 1);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) kr[t][s] = ld16_stream(kp + (key * HD + 32 * s + ko));
-    }
-  };
-  auto load_v = [&](int it) {
-    const int kb = k_lo + WI * it + KW * wave;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const uint32_t key = (uint32_t)min(kb + vkey + KG * i, k_hi - 1);
-      vr[i] = ld16_stream(vp + (key * HD + vo));
-    }
-  };
-  load_k(0);
-  load_v(0);
-
+  // The queries, before any DMA is in flight.  Lanes past GC read head h0 and
+  // use zeros.
   const float qscale = 1.44269504088896341f / sqrtf((float)HD);
   u32x4 qb[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (r16 < GC) {
-      const float* qp = a.q + ((size_t)n * a.nh + h0 + r16) * HD + 32 * s + 8 * g4;
-      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qp);
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qp + 4);
-      float f[8];
+    const float* qp = a.q + ((size_t)n * a.nh + h0 + (r16 < GC ? r16 : 0)) * HD + 32 * s + 8 * g4;
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(qp);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(qp + 4);
+    float f[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[e] = q0[e] * qscale;
-        f[e + 4] = q1[e] * qscale;
-      }
-      qb[s] = pack16<KVDT>(f);
-    } else {
-      qb[s] = zero;
+    for (int e = 0; e < 4; ++e) {
+      f[e] = q0[e] * qscale;
+      f[e + 4] = q1[e] * qscale;
     }
+    qb[s] = r16 < GC ? pack16<KVDT>(f) : zero;
   }
 
-  __shared__ float s_p[4][KW][GC];   // per wave: P of the current iteration
-  __shared__ float s_alpha[4][GC];   // per wave: rescale of the running sums
-  __shared__ float s_m[4][GC], s_l[4][GC];
-  __shared__ float s_acc[4][GC][HD];
+  // Rows past the chunk's end read the last valid row (finite values whose
+  // scores are masked and whose P is zero).  Iteration it uses buffer it & 1
+  // and refills it with iteration it + 2 once consumed; every iteration
+  // issues the same 2 TI loads (past the end they repeat the last row), so
+  // the wait counts below are exact.  DMA instruction i fills rows
+  // RPI i + l / CPR; lane l fetches the row's logical chunk (l % CPR) ^ swz.
+  auto load_tile = [&](const T* src, uint8_t* dst, int it, bool is_k) {
+    const int kb = k_lo + WI * it + KW * wave;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int r = i * RPI + lane / CPR;
+      const uint32_t key = (uint32_t)min(kb + r, k_hi - 1);
+      const int c = (lane % CPR) ^ (is_k ? (r & (CPR - 1)) : 2 * (r & 3));
+      dma16_stream(src + (key * HD + c * 8), dst + i * 1024);
+    }
+  };
+  // K fragment of slice s: row r16, logical chunk 4s + g4.
+  auto k_operand = [&](int buf, int s) {
+    return ld16(kring + buf * TILE + r16 * ROW + (((4 * s + g4) ^ (r16 & (CPR - 1))) << 4));
+  };
+  // Transposed V read for output tile t: lane (g4, 4e + q) points at row
+  // 4 g4 + e, dims 16 t + 4q .. +3.  (Inline assembly: for the builtin the
+  // compiler cannot tell these reads from reads of rows still in flight and
+  // waits for every outstanding load first.  The caller waits for the
+  // results itself.)
+  const int e4 = r16 >> 2, q4 = r16 & 3;
+  const uint32_t vaddr = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)vring +
+                         (4 * g4 + e4) * ROW + 8 * (q4 & 1);
+  auto v_operand = [&](int buf, int t) {
+    const uint32_t addr = vaddr + buf * TILE + (((2 * t + (q4 >> 1)) ^ (2 * e4)) << 4);
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+  };
+  load_tile(kp, kring, 0, true);
+  load_tile(vp, vring, 0, false);
+  load_tile(kp, kring + TILE, 1, true);
+  load_tile(vp, vring + TILE, 1, false);
 
   float m_run = -INFINITY;  // running max of head r16 over this wave's keys
   float l_run = 0.f;        // this lane's share of the running sum
-  float acc[GC][8];
+  f32x4 o[ND];              // lane: dim 16t + r16 of heads 4 g4 + 0..3
 #pragma unroll
-  for (int h = 0; h < GC; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int t = 0; t < ND; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = 0; it < nit; ++it) {
+  // One iteration; past nit every key is masked and it changes nothing.
+  auto iteration = [&](int it, int buf) {
     const int kb = k_lo + WI * it + KW * wave;
-    // Scores: lane holds head r16, keys kb + 16t + 4 g4 + i.
-    f32x4 sc[TW];
+    // K(it) has landed once only V(it), K(it+1) and V(it+1) may be outstanding.
+    wait_vmcnt<3 * TI>();
+    __builtin_amdgcn_sched_barrier(0);
+    // Scores: lane holds head r16, keys kb + 4 g4 + i.
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) c = mfma16_chunk<KVDT>(k_operand(buf, s), qb[s], c);
+    // The fragment reads are done before the K buffer is refilled.
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(kp, kring + buf * TILE, it + 2, true);
     float mt = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) c = mfma16_chunk<KVDT>(kr[t][s], qb[s], c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kb + 16 * t + 4 * g4 + i >= k_hi) c[i] = -INFINITY;
-        mt = fmaxf(mt, c[i]);
-      }
-      sc[t] = c;
+    for (int i = 0; i < 4; ++i) {
+      if (kb + 4 * g4 + i >= k_hi) c[i] = -INFINITY;
+      mt = fmaxf(mt, c[i]);
     }
-    if (it + 1 < nit) load_k(it + 1);
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     // No valid key yet for this wave: keep everything at zero.
     const bool none = (m_new == -INFINITY);
     const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float pf[4];
     float ls = 0.f;
 #pragma unroll
-    for (int t = 0; t < TW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sc[t][i] - m_new);
-        ls += p;
-        if (r16 < GC) s_p[wave][16 * t + 4 * g4 + i][r16] = p;
-      }
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = none ? 0.f : __builtin_amdgcn_exp2f(c[i] - m_new);
+      ls += pf[i];
+    }
     l_run = l_run * alpha + ls;
     m_run = m_new;
-    if (g4 == 0 && r16 < GC) s_alpha[wave][r16] = alpha;
-    // (This wave's LDS writes above are seen by its reads below: one wave's
-    // LDS instructions complete in order.)
-    float al[GC];
+    // Rescale factors of heads 4 g4 + 0..3 (held by lanes r16 = head); this
+    // wave's LDS accesses complete in order.
+    if (g4 == 0) s_alpha[wave * 16 + r16] = alpha;
+    const f32x4 al = *reinterpret_cast<const f32x4*>(&s_alpha[wave * 16 + 4 * g4]);
 #pragma unroll
-    for (int h = 0; h < GC; h += 4) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&s_alpha[wave][h]);
-      al[h] = a4[0]; al[h + 1] = a4[1]; al[h + 2] = a4[2]; al[h + 3] = a4[3];
-    }
+    for (int t = 0; t < ND; ++t) o[t] *= al;
+    u32x2 pa;
+    pa[0] = (uint32_t)Elt<KVDT>::from_f32(pf[0]) | ((uint32_t)Elt<KVDT>::from_f32(pf[1]) << 16);
+    pa[1] = (uint32_t)Elt<KVDT>::from_f32(pf[2]) | ((uint32_t)Elt<KVDT>::from_f32(pf[3]) << 16);
+    // V(it) has landed once only K(it+1), V(it+1) and K(it+2) may be outstanding.
+    wait_vmcnt<3 * TI>();
+    __builtin_amdgcn_sched_barrier(0);
+    u32x2 vb[ND];
 #pragma unroll
-    for (int h = 0; h < GC; ++h)
+    for (int t = 0; t < ND; ++t) vb[t] = v_operand(buf, t);
+    wait_lgkmcnt0();  // the transposed reads have landed (and the buffer may be refilled)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      float vf[8];
-      unpack16<KVDT>(vr[i], vf);
-      float p[GC];
-#pragma unroll
-      for (int h = 0; h < GC; h += 4) {
-        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[wave][vkey + KG * i][h]);
-        p[h] = p4[0]; p[h + 1] = p4[1]; p[h + 2] = p4[2]; p[h + 3] = p4[3];
-      }
-#pragma unroll
-      for (int h = 0; h < GC; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] += p[h] * vf[e];
-      // Bounds how far the scheduler hoists the P reads and V unpacks (each
-      // key's 16 values would otherwise stay live at once).
-      if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    if (it + 1 < nit) load_v(it + 1);
+    for (int t = 0; t < ND; ++t) o[t] = mfma16k16<KVDT>(pa, vb[t], o[t]);
+    load_tile(vp, vring + buf * TILE, it + 2, false);
+  };
+  for (int it = 0; it < nit; it += 2) {
+    iteration(it, 0);
+    iteration(it + 1, 1);
   }
 
-  // This wave's totals: acc over the lanes holding the same dims, l over the
-  // four lanes of each head.
-#pragma unroll
-  for (int h = 0; h < GC; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int o = DGN; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+  // This wave's totals (l over the four lanes of each head); the rings are
+  // reused once every wave's loads have landed.
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (lane < DGN) {
+  wait_vmcnt<0>();
+  __syncthreads();
 #pragma unroll
-    for (int h = 0; h < GC; ++h)
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g4 + i;
+    if (h < GC) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][h][vdg * 8 + e] = acc[h][e];
+      for (int t = 0; t < ND; ++t) s_acc[(wave * GC + h) * HD + 16 * t + r16] = o[t][i];
+    }
   }
-  if (g4 == 0 && r16 < GC) {
-    s_m[wave][r16] = m_run;
-    s_l[wave][r16] = l_run;
+  if (g4 == 0) {
+    s_m[wave * 16 + r16] = m_run;
+    s_l[wave * 16 + r16] = l_run;
   }
   __syncthreads();
   // Combine the waves (wave 0 always holds a valid key, so M is finite).
   for (int idx = tid; idx < GC * HD; idx += 256) {
     const int h = idx / HD, d = idx - h * HD;
-    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    const float M = fmaxf(fmaxf(s_m[h], s_m[16 + h]), fmaxf(s_m[32 + h], s_m[48 + h]));
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      if (s_m[w][h] != -INFINITY) v += exp2f(s_m[w][h] - M) * s_acc[w][h][d];
+      if (s_m[w * 16 + h] != -INFINITY) v += exp2f(s_m[w * 16 + h] - M) * s_acc[(w * GC + h) * HD + d];
     a.part_acc[(((size_t)n * a.nh + h0 + h) * a.nsplit + split) * HD + d] = v;
   }
   if (tid < GC) {
-    const float M = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
+    const float M = fmaxf(fmaxf(s_m[tid], s_m[16 + tid]), fmaxf(s_m[32 + tid], s_m[48 + tid]));
     float l = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      if (s_m[w][tid] != -INFINITY) l += exp2f(s_m[w][tid] - M) * s_l[w][tid];
+      if (s_m[w * 16 + tid] != -INFINITY) l += exp2f(s_m[w * 16 + tid] - M) * s_l[w * 16 + tid];
     const size_t pi = ((size_t)n * a.nh + h0 + tid) * a.nsplit + split;
     a.part_m[pi] = M;
     a.part_l[pi] = l;

@@ -168,6 +168,22 @@ __device__ __forceinline__ f32x4 mfma16_chunk(u32x4 a, u32x4 b, f32x4 acc) {
   }
 }
 
+// 16x16x16 bf16/f16 MFMA: the same 16x16 result layout as above; A lane l:
+// row l%16, B lane l: column l%16, each with the 4 k-elements of k-group l/16
+// (one 8-byte register pair).
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 acc) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, a),
+                                                     __builtin_bit_cast(v4i16, b), acc, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), acc, 0, 0, 0);
+  }
+}
+
 // 32x32x16 bf16/f16 MFMA: lane l holds column l%32 and rows
 // (r/4)*8 + (l/32)*4 + r%4 of the result, r = 0..15; A lane l: row l%32,
 // B lane l: column l%32, each with the 8 k-elements of k-group l/32.

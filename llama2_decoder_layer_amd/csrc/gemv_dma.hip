@@ -14,7 +14,7 @@
 // ds_read_b128 cycle serves land in 16 distinct 4-bank groups.
 //
 // Few row blocks (O, down, QKV at batch 32) leave CUs idle, so the K range is
-// split over a second grid dimension; each split writes float32 partials and a
+// split over several workgroups; each split writes float32 partials and a
 // small kernel sums them and applies the epilogue.  One split applies the
 // epilogue directly: residual add, SwiGLU, RoPE + KV append, or logits.
 #include "common.cuh"
@@ -75,7 +75,7 @@ __device__ __forceinline__ void sk_store4(const ProjArgs& a, int m, int f, const
 }
 
 template <int DT, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, int kchunk) {
+__global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, int kchunk, int nsplit) {
   typedef typename Elt<DT>::T T;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int FB = SWI ? SK_BM / 2 : SK_BM;  // features per workgroup
@@ -87,8 +87,11 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = a.K;
-  const int f0 = blockIdx.x * FB;
-  const int k0 = blockIdx.y * kchunk;
+  // Grid x enumerates (row block, K split) with the split fastest, so the
+  // workgroups resident together cover neighbouring K ranges of the same rows.
+  const int blk = blockIdx.x / nsplit, ks = blockIdx.x - blk * nsplit;
+  const int f0 = blk * FB;
+  const int k0 = ks * kchunk;
   const int nkt = (min(K, k0 + kchunk) - k0) / SK_BK;
 
   // DMA: instruction i of a stage fills rows 8i..8i+7 (i < 8: weights, else
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   if constexpr (SPLIT) {
     if (m < a.M) {
       const int nrows = SWI ? 2 * a.N : a.N;
-      float* p = part + ((size_t)blockIdx.y * a.M + m) * nrows;
+      float* p = part + ((size_t)ks * a.M + m) * nrows;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r = rb * 32 + g * 8 + h2 * 4;
@@ -261,12 +264,13 @@ static hipError_t gemv_dma_epi(const ProjArgs& a, hipStream_t s) {
   const int ns = sk_split(EPI, a.N, a.K, &kchunk);
   const int nblk = (a.N + sk_features(EPI) - 1) / sk_features(EPI);
   if (ns == 1) {
-    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false>), dim3(nblk, 1), dim3(256), 0, s, a,
-              (float*)nullptr, kchunk);
+    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false>), dim3(nblk), dim3(256), 0, s, a,
+              (float*)nullptr, kchunk, 1);
     return hipGetLastError();
   }
   if (!a.part) return hipErrorInvalidValue;
-  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true>), dim3(nblk, ns), dim3(256), 0, s, a, a.part, kchunk);
+  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true>), dim3(nblk * ns), dim3(256), 0, s, a, a.part, kchunk,
+            ns);
   const int n = ((a.N + 3) / 4) * a.M;
   LL_LAUNCH((gemv_split_reduce_kernel<DT, EPI>), dim3((n + 255) / 256), dim3(256), 0, s, a,
             (const float*)a.part, ns);
