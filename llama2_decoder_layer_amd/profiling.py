@@ -39,11 +39,11 @@ CSRC = os.path.join(PKG, "csrc")
 # the source files they are compiled from.
 _COMMON = ["common.cuh", "epilogue.cuh", "kernels.h"]
 KERNELS = {
-    "gemv_gate_up": (r"gemv_\w+_kernel<\d+, 2,", ["gemv.hip"] + _COMMON),
+    "gemv_gate_up": (r"gemv_\w+_kernel<\d+, 2,", ["gemv.hip", "gemv_dma.hip"] + _COMMON),
     "gemm_gate_up": (r"gemm_(dma_)?kernel<\d+, 2,", ["gemm.hip"] + _COMMON),
     "gemm_qkv": (r"gemm_(dma_)?kernel<\d+, 0,", ["gemm.hip"] + _COMMON),
-    "attn_prefill": (r"attn_prefill_kernel<", ["attn_prefill.hip"] + _COMMON),
-    "attn_decode": (r"attn_split_kernel<", ["attn_decode.hip"] + _COMMON),
+    "attn_prefill": (r"attn_prefill(_tr)?_kernel<", ["attn_prefill.hip"] + _COMMON),
+    "attn_decode": (r"attn_(split|gqa)_kernel<", ["attn_decode.hip"] + _COMMON),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 NOTE = "(REPO is the repository root, OUT the output directory.)"
