@@ -134,6 +134,14 @@ def test_bf16_decode_gqa_f16_cache():
                     [0, 1, 63, 64, 65, 300, 511], 512, 110)
 
 
+def test_bf16_decode_gqa8_hd64_long():
+    # 8 query heads per KV head at head_dim 64 (the MFMA decode attention with
+    # GC = 8, HD = 64), contexts from one key to several chunks, odd and even
+    # numbers of 64-key steps per workgroup
+    run_decode_case("bf16-decode-gqa8-hd64", S.Shape(512, 8, 1, 64, 1376), "bf16", "f16",
+                    [0, 15, 16, 17, 129, 255, 256, 1000, 2998], 3000, 113)
+
+
 def test_bf16_decode_batch_over_32():
     ctx = list(np.random.Generator(np.random.PCG64(5)).integers(0, 200, 40))
     run_decode_case("bf16-decode-b40", S.Shape(256, 4, 1, 64, 688), "bf16", "bf16", ctx, 256, 111)
