@@ -357,8 +357,8 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < ND; ++t) o[t] *= al;
     u32x2 pa;
-    pa[0] = (uint32_t)Elt<KVDT>::from_f32(pf[0]) | ((uint32_t)Elt<KVDT>::from_f32(pf[1]) << 16);
-    pa[1] = (uint32_t)Elt<KVDT>::from_f32(pf[2]) | ((uint32_t)Elt<KVDT>::from_f32(pf[3]) << 16);
+    pa[0] = pack2<KVDT>(pf[0], pf[1]);
+    pa[1] = pack2<KVDT>(pf[2], pf[3]);
     // V(it) has landed once only K(it+1), V(it+1) and K(it+2) may be outstanding.
     wait_vmcnt<3 * TI>();
     __builtin_amdgcn_sched_barrier(0);

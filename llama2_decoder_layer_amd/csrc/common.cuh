@@ -91,6 +91,21 @@ __device__ __forceinline__ void unpack16(u32x4 c, float* f) {
   }
 }
 
+// Two floats to two 16-bit elements of one 32-bit word (a in the low half),
+// rounded to nearest even: one v_cvt_pk_{bf16,f16}_f32.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  if constexpr (DT == DT_BF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+}
+
 // Pack PER16 floats into one chunk.
 template <int DT>
 __device__ __forceinline__ u32x4 pack16(const float* f) {
@@ -100,11 +115,7 @@ __device__ __forceinline__ u32x4 pack16(const float* f) {
     for (int i = 0; i < 4; ++i) c[i] = __float_as_uint(f[i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = Elt<DT>::from_f32(f[2 * i]);
-      uint32_t hi = Elt<DT>::from_f32(f[2 * i + 1]);
-      c[i] = lo | (hi << 16);
-    }
+    for (int i = 0; i < 4; ++i) c[i] = pack2<DT>(f[2 * i], f[2 * i + 1]);
   }
   return c;
 }
@@ -123,8 +134,8 @@ __device__ __forceinline__ void store4(typename Elt<DT>::T* p, float a, float b,
     *reinterpret_cast<f32x4*>(p) = v;
   } else {
     u32x2 v;
-    v[0] = (uint32_t)Elt<DT>::from_f32(a) | ((uint32_t)Elt<DT>::from_f32(b) << 16);
-    v[1] = (uint32_t)Elt<DT>::from_f32(c) | ((uint32_t)Elt<DT>::from_f32(d) << 16);
+    v[0] = pack2<DT>(a, b);
+    v[1] = pack2<DT>(c, d);
     *reinterpret_cast<u32x2*>(p) = v;
   }
 }
