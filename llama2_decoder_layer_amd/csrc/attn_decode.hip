@@ -291,18 +291,12 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
     return ld16(kring + buf * TILE + r16 * ROW + (((4 * s + g4) ^ (r16 & (CPR - 1))) << 4));
   };
   // Transposed V read for output tile t: lane (g4, 4e + q) points at row
-  // 4 g4 + e, dims 16 t + 4q .. +3.  (Inline assembly: for the builtin the
-  // compiler cannot tell these reads from reads of rows still in flight and
-  // waits for every outstanding load first.  The caller waits for the
-  // results itself.)
+  // 4 g4 + e, dims 16 t + 4q .. +3 (ds_read_tr16: the caller waits for the
+  // results itself).
   const int e4 = r16 >> 2, q4 = r16 & 3;
-  const uint32_t vaddr = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)vring +
-                         (4 * g4 + e4) * ROW + 8 * (q4 & 1);
+  const uint32_t vaddr = lds_addr(vring) + (4 * g4 + e4) * ROW + 8 * (q4 & 1);
   auto v_operand = [&](int buf, int t) {
-    const uint32_t addr = vaddr + buf * TILE + (((2 * t + (q4 >> 1)) ^ (2 * e4)) << 4);
-    u32x2 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
+    return ds_read_tr16(vaddr + buf * TILE + (((2 * t + (q4 >> 1)) ^ (2 * e4)) << 4));
   };
   load_tile(kp, kring, 0, true);
   load_tile(vp, vring, 0, false);

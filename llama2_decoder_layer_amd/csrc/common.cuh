@@ -23,6 +23,15 @@ constexpr int WAVE = 64;
 // Compile-time index (register-ring slots and unrolled loop parities).
 template <int I>
 using ic = std::integral_constant<int, I>;
+// Calls f(ic<I>{}), ..., f(ic<N-1>{}): a loop whose index is a compile-time
+// constant in the body.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Scalar conversions.  float -> bf16/f16 round to nearest even.
@@ -225,6 +234,23 @@ __device__ __forceinline__ void dma16_stream(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 2);
 }
 
+// ds_read_b64_tr_b16 at LDS byte address addr, as inline assembly: within each
+// group of 16 lanes, lane i = 4e + q points at 4 16-bit elements (row R + e,
+// cols C + 4q .. +3) and lane j receives rows R .. R+3 of col C + j.  The
+// compiler does not track this read: the caller waits for it (lgkmcnt) before
+// using the result.  (For the builtin the compiler cannot tell the read from
+// reads of rows a global_load_lds still has in flight, and waits for every
+// outstanding load first.)
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
@@ -235,6 +261,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) only (vmcnt and expcnt at their maxima).
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+// s_waitcnt lgkmcnt(N) only: at most N LDS/scalar-memory operations still
+// outstanding (LDS operations of one wave complete in order).
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
 }
 
 // ---------------------------------------------------------------------------

@@ -365,14 +365,6 @@ struct DmaPipe {
   static constexpr int NST = (BK == 64) ? 2 : 4;
 };
 
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(ic<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // Workgroups [0, full_tiles) each take a whole tile.  When the tiles do not
 // fill a whole number of rounds over the CUs, the remaining tiles are split
 // along K into ksplit parts, one workgroup each, so the last round is full;
