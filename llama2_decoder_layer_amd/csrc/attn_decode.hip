@@ -202,24 +202,26 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnDecodeArgs a) {
 // lanes of a transposed read hit 16 bank pairs); the swizzle is applied on
 // the global side, since the DMA writes each instruction's 1 KB linearly.
 // Queries and P are rounded to the cache format for the MFMAs.  Output: the
-// same partials as attn_split_kernel, one split per CH = 64 NIT keys.
-template <int KVDT, int HD, int GC, int NIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// same partials as attn_split_kernel, one split per a.chunk keys; with a
+// single split (a whole context per workgroup) the normalised output itself,
+// and no merge follows.  NW waves per workgroup: 4 for split contexts, 8 for
+// whole ones.
+template <int KVDT, int HD, int GC, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_gqa_kernel(AttnDecodeArgs a) {
   typedef typename Elt<KVDT>::T T;
   constexpr int NS = HD / 32;         // 32-dim slices: score MFMAs per tile
   constexpr int ND = HD / 16;         // 16-dim output tiles: P V MFMAs per tile
   constexpr int KW = 16;              // keys per wave and iteration
-  constexpr int WI = 4 * KW;          // keys per workgroup and iteration
-  constexpr int CH = WI * NIT;        // keys per workgroup
+  constexpr int WI = NW * KW;         // keys per workgroup and iteration
   constexpr int ROW = HD * 2;         // bytes of one K or V row
   constexpr int TILE = KW * ROW;      // one wave's K (or V) rows of one iteration
   constexpr int TI = TILE / 1024;     // DMA instructions per tile
   constexpr int RPI = 1024 / ROW;     // rows per DMA instruction
   constexpr int CPR = ROW / 16;       // 16-byte chunks per row
   constexpr int WAVE_LDS = 4 * TILE;  // K and V rings of one wave
-  constexpr int RING = 4 * WAVE_LDS;
-  static_assert(4 * GC * HD * 4 <= RING, "the wave sums reuse the rings");
+  constexpr int RING = NW * WAVE_LDS;
+  static_assert(NW * GC * HD * 4 <= RING, "the wave sums reuse the rings");
   const int split = blockIdx.x;
   const int g = a.nh / a.nkv;
   const int per_kv = g / GC;
@@ -228,8 +230,8 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
   const int n = blockIdx.z;
   int b;
   const int pos = query_position(a, n, &b);
-  const int k_lo = split * CH;
-  const int k_hi = min(k_lo + CH, pos + 1);
+  const int k_lo = split * a.chunk;
+  const int k_hi = min(k_lo + a.chunk, pos + 1);
   if (k_lo >= k_hi) return;  // past this query's context: not counted, not merged
   const int nit = (k_hi - k_lo + WI - 1) / WI;
 
@@ -237,11 +239,11 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
   // outstanding load before each LDS read): per-wave K and V rings, then
   // per-wave rescale factors, maxima and sums.  The cross-wave sums reuse the
   // rings.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + 3 * 4 * 16 * 4];
-  float* s_alpha = reinterpret_cast<float*>(lds + RING);  // [4][16]
-  float* s_m = s_alpha + 64;                              // [4][16]
-  float* s_l = s_m + 64;                                  // [4][16]
-  float* s_acc = reinterpret_cast<float*>(lds);           // [4][GC][HD] after the loop
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + 3 * NW * 16 * 4];
+  float* s_alpha = reinterpret_cast<float*>(lds + RING);  // [NW][16]
+  float* s_m = s_alpha + NW * 16;                         // [NW][16]
+  float* s_l = s_m + NW * 16;                             // [NW][16]
+  float* s_acc = reinterpret_cast<float*>(lds);           // [NW][GC][HD] after the loop
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -390,24 +392,38 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
   }
   __syncthreads();
   // Combine the waves (wave 0 always holds a valid key, so M is finite).
-  for (int idx = tid; idx < GC * HD; idx += 256) {
+  auto wave_max_m = [&](int h) {
+    float M = s_m[h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + h]);
+    return M;
+  };
+  for (int idx = tid; idx < GC * HD; idx += NW * 64) {
     const int h = idx / HD, d = idx - h * HD;
-    const float M = fmaxf(fmaxf(s_m[h], s_m[16 + h]), fmaxf(s_m[32 + h], s_m[48 + h]));
-    float v = 0.f;
+    const float M = wave_max_m(h);
+    float v = 0.f, l = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      if (s_m[w * 16 + h] != -INFINITY) v += exp2f(s_m[w * 16 + h] - M) * s_acc[(w * GC + h) * HD + d];
-    a.part_acc[(((size_t)n * a.nh + h0 + h) * a.nsplit + split) * HD + d] = v;
-  }
-  if (tid < GC) {
-    const float M = fmaxf(fmaxf(s_m[tid], s_m[16 + tid]), fmaxf(s_m[32 + tid], s_m[48 + tid]));
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      if (s_m[w * 16 + tid] != -INFINITY) l += exp2f(s_m[w * 16 + tid] - M) * s_l[w * 16 + tid];
-    const size_t pi = ((size_t)n * a.nh + h0 + tid) * a.nsplit + split;
-    a.part_m[pi] = M;
-    a.part_l[pi] = l;
+    for (int w = 0; w < NW; ++w)
+      if (s_m[w * 16 + h] != -INFINITY) {
+        const float sc = exp2f(s_m[w * 16 + h] - M);
+        v += sc * s_acc[(w * GC + h) * HD + d];
+        l += sc * s_l[w * 16 + h];
+      }
+    if (a.nsplit == 1) {
+      // The whole context: the normalised output (no merge follows).
+      const size_t oi = (size_t)n * a.nh * HD + (size_t)(h0 + h) * HD + d;
+      const float o = v / l;
+      if (a.act_dt == DT_F32) reinterpret_cast<float*>(a.o)[oi] = o;
+      else if (a.act_dt == DT_BF16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(o);
+      else reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_f16(o);
+    } else {
+      a.part_acc[(((size_t)n * a.nh + h0 + h) * a.nsplit + split) * HD + d] = v;
+      if (d == 0) {
+        const size_t pi = ((size_t)n * a.nh + h0 + h) * a.nsplit + split;
+        a.part_m[pi] = M;
+        a.part_l[pi] = l;
+      }
+    }
   }
 }
 
@@ -489,13 +505,10 @@ static hipError_t split_launch_kpt(const AttnDecodeArgs& a, dim3 grid, hipStream
 
 template <int KVDT, int HD, int GC>
 static hipError_t gqa_launch_tw(const AttnDecodeArgs& a, dim3 grid, hipStream_t s) {
-  switch (a.chunk / 64) {
-    case 4: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 8>), grid, dim3(256), 0, s, a); break;
-    case 16: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 16>), grid, dim3(256), 0, s, a); break;
-    case 32: LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 32>), grid, dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (a.nsplit == 1)
+    LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 8>), grid, dim3(512), 0, s, a);
+  else
+    LL_LAUNCH((attn_gqa_kernel<KVDT, HD, GC, 4>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -528,7 +541,11 @@ int attn_pick_chunk(int hd, int max_keys, int queries, int nkv, int g, int kv_dt
   const int gc = attn_heads_per_group(g);
   const int groups = nkv * (g / gc);
   if (attn_uses_gqa_kernel(kv_dt, g)) {
-    // Chunk 256, 512, 1024 or 2048 keys: the largest that still gives >= 512
+    // With a workgroup per CU or more at one split per query and group, whole
+    // contexts (8-wave workgroups, no merge launch); the longest context then
+    // sets the time as it does with 2048-key chunks.
+    if ((int64_t)queries * groups >= 256) return (max_keys + 127) / 128 * 128;
+    // Otherwise chunks of 256, 512, 1024 or 2048 keys: the largest that still gives >= 512
     // workgroups (counted at the longest context).  Longer chunks mean fewer
     // partials to merge and fewer per-workgroup tails; measured on the 70B
     // batch-32 decode, 2048 beats both 1024 and 4096.
@@ -584,6 +601,8 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
       : (a.kv_dt == DT_BF16) ? split_launch<DT_BF16, 64>(a, s) : split_launch<DT_F16, 64>(a, s);
   }
   if (e != hipSuccess) return e;
+  // A single split of the GQA kernel wrote the output itself.
+  if (a.nsplit == 1 && attn_uses_gqa_kernel(a.kv_dt, a.nh / a.nkv)) return hipSuccess;
   return a.hd == 128 ? merge_launch<128>(a, s) : merge_launch<64>(a, s);
 }
 
