@@ -91,21 +91,22 @@ def random_layer(shape: S.Shape, act: str, seed: int) -> dict:
     return S.draw_layer(np.random.SeedSequence(seed), shape, act)
 
 
-# Two half-ulps, relative, of the format the layer stores out and h1 in: the
-# stored result carries that much rounding whatever the kernels compute.
+# Half an ulp, relative to the value, of the format the layer stores out and
+# h1 in (8, 11 and 24 significant bits): each stored tensor carries up to that
+# much rounding whatever the kernels compute.
 STORE_ULP = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 
 
 def delta_error(got, want, x, act: str):
     """(error, allowance) of the branch delta out - x.  out and h1 are stored
     in `act`, so each carries up to half an ulp of |out| of rounding that is no
-    branch error; the allowance adds those two half-ulps, relative to the
-    branch scale."""
+    branch error; the allowance adds those two half-ulps (STORE_ULP is one
+    half-ulp relative to the value), relative to the branch scale."""
     dg = np.asarray(got) - x
     dw = np.asarray(want) - x
     scale = max(np.max(np.abs(dw)), 1e-30)
     err = rel_err(dg, dw)
-    return err, STORE_ULP[act] * np.max(np.abs(want)) / scale
+    return err, 2.0 * STORE_ULP[act] * np.max(np.abs(want)) / scale
 
 
 def check_errors(label: str, errs: dict, tol: float, allow: dict | None = None) -> None:
