@@ -4,14 +4,18 @@
 // A workgroup owns 64 weight rows (SwiGLU: 32 gate + the 32 matching up rows)
 // and all token slots (32, the missing ones read token 0 and are dropped), over
 // one K range.  Weights and activations move global -> LDS by
-// global_load_lds in 64-k stages (128-byte row slices), NST stages deep, so
-// each workgroup keeps up to (NST-1) x 12 KB in flight without holding any of
-// it in registers.  The four waves split a stage's work as 2 row blocks x 2
+// global_load_lds in 256-k stages (512-byte row slices), three deep (144 KB of
+// LDS, one workgroup per CU), so each row has 1 KB in flight and each CU
+// 64 KB of weights.  The four waves split a stage's work as 2 row blocks x 2
 // k halves of v_mfma_f32_32x32x16; the k halves meet in LDS at the end.
+// Measured on the 70B gate/up at 32 tokens against 64-k stages four deep with
+// three workgroups per CU (128-byte slices, 384 bytes per row in flight):
+// 183 -> 173 us; 128-k stages six deep (one workgroup per CU) were slower
+// (196 us), three deep with two workgroups per CU in between (176 us).
 //
-// The 16-byte chunks of a 128-byte row slice are stored XOR-swizzled by
-// (row >> 1) & 7, which makes the fragment reads conflict-free: the 16 rows one
-// ds_read_b128 cycle serves land in 16 distinct 4-bank groups.
+// The 16-byte chunks of a row slice are stored XOR-swizzled by (row & 15),
+// which makes the fragment reads conflict-free: the 16 rows one ds_read_b128
+// cycle serves land in 16 distinct 4-bank groups.
 //
 // Few row blocks (O, down, QKV at batch 32) leave CUs idle, so the K range is
 // split over several workgroups; each split writes float32 partials and a
@@ -24,10 +28,8 @@ namespace ll {
 
 constexpr int SK_BM = 64;                          // weight rows per workgroup
 constexpr int SK_BN = 32;                          // token slots
-constexpr int SK_BK = 64;                          // k per stage
-constexpr int SK_NST = 4;                          // stages in LDS
-constexpr int SK_ROWB = SK_BK * 2;                 // bytes per row slice
-constexpr int SK_STAGE = (SK_BM + SK_BN) * SK_ROWB;  // 12 KB
+constexpr int SK_BK = 256;                         // k per stage
+constexpr int SK_NST = 3;                          // stages in LDS
 constexpr int SK_TARGET_WG = 512;                  // workgroups wanted per launch
 constexpr int SK_MAX_SPLIT = 8;
 
@@ -38,10 +40,10 @@ static int sk_split(int epi, int N, int K, int* kchunk) {
   const int nblk = (N + sk_features(epi) - 1) / sk_features(epi);
   int ns = (SK_TARGET_WG + nblk - 1) / nblk;
   ns = std::max(1, std::min(ns, SK_MAX_SPLIT));
-  const int nkt = K / SK_BK;
+  const int nkt = K / 64;
   ns = std::min(ns, nkt);
   const int kt_per = (nkt + ns - 1) / ns;
-  *kchunk = kt_per * SK_BK;
+  *kchunk = kt_per * 64;
   return (nkt + kt_per - 1) / kt_per;
 }
 
@@ -74,15 +76,40 @@ __device__ __forceinline__ void sk_store4(const ProjArgs& a, int m, int f, const
   }
 }
 
-template <int DT, int EPI, bool SPLIT>
+// Stage geometry for BK (k per stage: 64, 128 or 256) and NST stages in LDS.  A
+// row slice is BK*2 bytes = CPR 16-byte chunks; one global_load_lds (64 lanes
+// x 16 bytes) fills RPI whole row slices, so a stage takes NI instructions,
+// NIW per wave.  Chunk c of row r sits at physical chunk c ^ (r & 15): the 16
+// rows that one ds_read_b128 cycle serves then land in 16 distinct 4-bank
+// groups.
+template <int BK, int NST>
+struct SkGeom {
+  static_assert(BK == 64 || BK == 128 || BK == 256, "stage width");
+  static constexpr int ROWB = BK * 2;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int NI = (SK_BM + SK_BN) / RPI;
+  static constexpr int NIW = NI / 4;
+  static constexpr int NIW_W = (SK_BM / RPI) / 4;  // weight instructions per wave
+  static constexpr int STAGE = (SK_BM + SK_BN) * ROWB;
+  static constexpr int KS2 = BK / 32;              // 32x32x16 k-steps per wave per stage
+  static constexpr int LDS = NST * STAGE;
+  static_assert(NIW * (NST - 2) < 64, "vmcnt range");
+  // Physical chunk = logical chunk ^ swz(row).  128-byte slices put two rows
+  // in one 256-byte bank line, hence the shifted form for BK = 64.
+  static __device__ __forceinline__ int swz(int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & 7); }
+};
+
+template <int DT, int EPI, bool SPLIT, int BK, int NST>
 __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, int kchunk, int nsplit) {
   typedef typename Elt<DT>::T T;
+  typedef SkGeom<BK, NST> G;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int FB = SWI ? SK_BM / 2 : SK_BM;  // features per workgroup
   // One LDS object: the stage ring, reused at the end for the cross-wave sums.
   // (A second LDS variable gives the accesses alias scopes, and the wait-count
   // pass then waits for every outstanding DMA before each fragment read.)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[SK_NST * SK_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS];
   f32x16* red = reinterpret_cast<f32x16*>(lds);  // [2][64] after the k loop
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -92,20 +119,25 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   const int blk = blockIdx.x / nsplit, ks = blockIdx.x - blk * nsplit;
   const int f0 = blk * FB;
   const int k0 = ks * kchunk;
-  const int nkt = (min(K, k0 + kchunk) - k0) / SK_BK;
+  const int klen = min(K, k0 + kchunk) - k0;  // a multiple of 64
+  const int nkt = (klen + BK - 1) / BK;
 
-  // DMA: instruction i of a stage fills rows 8i..8i+7 (i < 8: weights, else
-  // tokens 8(i-8)..); wave w issues i = w, w+4 (weights) and w+8 (tokens).
-  // Lane l: row 8i + l/8, physical chunk l%8 = logical chunk ^ ((row>>1)&7).
-  const int rr = lane >> 3, pc = lane & 7;
-  const T* src[3];
+  // DMA: instruction i of a stage fills stage rows RPI*i .. RPI*i + RPI-1
+  // (rows 0..63 weights, 64..95 token slots); wave w issues i = w + 4j.  Lane
+  // l: row RPI*i + l/CPR, physical chunk l%CPR, logical chunk phys ^ (row&15).
+  // A chunk past the end of the K range (last stage of a range that is not a
+  // multiple of BK) re-reads the range's first chunk instead; the k-steps that
+  // would use it are skipped, and every wave still issues the same number of
+  // loads per stage, which the wait counts rely on.
+  const T* src[G::NIW];
+  int kofs[G::NIW];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
+  for (int j = 0; j < G::NIW; ++j) {
     const int i = wave + 4 * j;
-    const int r = 8 * (i & 7) + rr;
-    const int c = pc ^ ((r >> 1) & 7);
+    const int r = G::RPI * i + lane / G::CPR;
+    const int c = (lane % G::CPR) ^ G::swz(r);
     const T* row;
-    if (j < 2) {
+    if (r < SK_BM) {
       if constexpr (SWI) {
         const int f = f0 + (r & 31);
         row = reinterpret_cast<const T*>(r < 32 ? a.w[0] : a.w[1]) + (size_t)(f < a.N ? f : 0) * K;
@@ -114,59 +146,75 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
         row = seg_row<T>(a, f < a.N ? f : 0);
       }
     } else {
-      row = reinterpret_cast<const T*>(a.x) + (size_t)(r < a.M ? r : 0) * K;
+      const int m = r - SK_BM;
+      row = reinterpret_cast<const T*>(a.x) + (size_t)(m < a.M ? m : 0) * K;
     }
-    src[j] = row + k0 + c * 8;
+    src[j] = row + k0;
+    kofs[j] = c * 8;
   }
   auto issue = [&](int st, int kt) {
-    uint8_t* base = lds + st * SK_STAGE;
-    const int k = kt * SK_BK;
+    uint8_t* base = lds + st * G::STAGE;
+    const int k = kt * BK;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      if (j < 2) dma16_stream(src[j] + k, base + (wave + 4 * j) * 1024);  // weights
-      else dma16(src[j] + k, base + (wave + 4 * j) * 1024);               // activations
+    for (int j = 0; j < G::NIW; ++j) {
+      const int kk = k + kofs[j];
+      const T* g = src[j] + (kk < klen ? kk : 0);
+      uint8_t* d = base + (wave + 4 * j) * 1024;
+      if (j < G::NIW_W) dma16_stream(g, d);  // weights: instructions 0 .. 64/RPI - 1
+      else dma16(g, d);                      // activations
     }
   };
-  // This wave's part of a stage has landed once at most `newer` later stages
-  // (3 loads each) are outstanding.
+  // This wave's part of stage kt has landed once at most `newer` later stages
+  // (NIW loads each) are outstanding.
   auto wait_stage = [&](int newer) {
-    if (newer >= 2) wait_vmcnt<6>();
-    else if (newer == 1) wait_vmcnt<3>();
-    else wait_vmcnt<0>();
+    static_for<0, NST - 1>([&](auto n) {
+      if (newer == decltype(n)::value) wait_vmcnt<decltype(n)::value * G::NIW>();
+    });
   };
 
-  // Fragments: wave w multiplies row block rb = w & 1 over k-steps 2(w>>1)
-  // and 2(w>>1)+1 of every stage.
+  // Fragments: wave w multiplies row block rb = w & 1 over the k-steps
+  // kh*KS2 .. kh*KS2 + KS2-1 (kh = w >> 1) of every stage.
   const int rb = wave & 1, kh = wave >> 1;
   const int l32 = lane & 31, h2 = lane >> 5;
-  const int swz = (l32 >> 1) & 7;
-  const int aoff = (rb * 32 + l32) * SK_ROWB;
-  const int boff = SK_BM * SK_ROWB + l32 * SK_ROWB;
-  const int ch0 = (((4 * kh + 0 + h2) ^ swz) * 16);  // k-step 2kh: logical chunk 2(2kh)+h2
-  const int ch1 = (((4 * kh + 2 + h2) ^ swz) * 16);  // k-step 2kh+1
+  const int swz = G::swz(l32);  // rows rb*32 + l32 and token row 64 + l32 share it
+  const int aoff = (rb * 32 + l32) * G::ROWB;
+  const int boff = SK_BM * G::ROWB + l32 * G::ROWB;
 
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 
 #pragma unroll
-  for (int st = 0; st < SK_NST - 1; ++st)
+  for (int st = 0; st < NST - 1; ++st)
     if (st < nkt) issue(st, st);
   // The barrier is a bare s_barrier: a full __syncthreads would also wait for
   // the stages still in flight.  Its explicit waits: this wave's loads of stage
   // kt (vmcnt) and its reads of stage kt-1, which the MFMAs consumed.  The
   // sched_barriers keep the fragment reads below it.
   for (int kt = 0; kt < nkt; ++kt) {
-    wait_stage(min(nkt - 1, kt + SK_NST - 2) - kt);
+    wait_stage(min(nkt - 1, kt + NST - 2) - kt);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();  // stage kt complete everywhere; stage kt-1 no longer read
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + SK_NST - 1 < nkt) issue((kt + SK_NST - 1) % SK_NST, kt + SK_NST - 1);
-    const uint8_t* base = lds + (kt % SK_NST) * SK_STAGE;
-    const u32x4 a0 = ld16(base + aoff + ch0), b0 = ld16(base + boff + ch0);
-    const u32x4 a1 = ld16(base + aoff + ch1), b1 = ld16(base + boff + ch1);
-    acc = mfma32<DT>(a0, b0, acc);
-    acc = mfma32<DT>(a1, b1, acc);
+    if (kt + NST - 1 < nkt) issue((kt + NST - 1) % NST, kt + NST - 1);
+    const uint8_t* base = lds + (kt % NST) * G::STAGE;
+    const int nvalid = (klen - kt * BK) / 16 - kh * G::KS2;  // k-steps of this wave with data
+    if (nvalid >= G::KS2) {
+      u32x4 fa[G::KS2], fb[G::KS2];
+#pragma unroll
+      for (int t = 0; t < G::KS2; ++t) {
+        const int ch = ((2 * (kh * G::KS2 + t) + h2) ^ swz) * 16;
+        fa[t] = ld16(base + aoff + ch);
+        fb[t] = ld16(base + boff + ch);
+      }
+#pragma unroll
+      for (int t = 0; t < G::KS2; ++t) acc = mfma32<DT>(fa[t], fb[t], acc);
+    } else {
+      for (int t = 0; t < nvalid; ++t) {
+        const int ch = ((2 * (kh * G::KS2 + t) + h2) ^ swz) * 16;
+        acc = mfma32<DT>(ld16(base + aoff + ch), ld16(base + boff + ch), acc);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -248,33 +296,38 @@ __global__ __launch_bounds__(256) void gemv_split_reduce_kernel(ProjArgs a, cons
 }
 
 size_t gemv_dma_partial_floats(int epi, int N, int K, int M) {
-  if (K % SK_BK != 0 || M < 1 || M > SK_BN) return 0;
+  if (K % 64 != 0 || M < 1 || M > SK_BN) return 0;
   int kchunk;
   const int ns = sk_split(epi, N, K, &kchunk);
   return ns > 1 ? (size_t)ns * M * sk_rows(epi, N) : 0;
 }
 
 bool gemv_dma_supported(int dt, int M, int K, int N) {
-  return dt != DT_F32 && M >= 1 && M <= SK_BN && K % SK_BK == 0 && N % 4 == 0;
+  return dt != DT_F32 && M >= 1 && M <= SK_BN && K % 64 == 0 && N % 4 == 0;
 }
 
-template <int DT, int EPI>
-static hipError_t gemv_dma_epi(const ProjArgs& a, hipStream_t s) {
+template <int DT, int EPI, int BK, int NST>
+static hipError_t gemv_dma_cfg(const ProjArgs& a, hipStream_t s) {
   int kchunk;
   const int ns = sk_split(EPI, a.N, a.K, &kchunk);
   const int nblk = (a.N + sk_features(EPI) - 1) / sk_features(EPI);
   if (ns == 1) {
-    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false>), dim3(nblk), dim3(256), 0, s, a,
+    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false, BK, NST>), dim3(nblk), dim3(256), 0, s, a,
               (float*)nullptr, kchunk, 1);
     return hipGetLastError();
   }
   if (!a.part) return hipErrorInvalidValue;
-  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true>), dim3(nblk * ns), dim3(256), 0, s, a, a.part, kchunk,
-            ns);
+  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true, BK, NST>), dim3(nblk * ns), dim3(256), 0, s, a, a.part,
+            kchunk, ns);
   const int n = ((a.N + 3) / 4) * a.M;
   LL_LAUNCH((gemv_split_reduce_kernel<DT, EPI>), dim3((n + 255) / 256), dim3(256), 0, s, a,
             (const float*)a.part, ns);
   return hipGetLastError();
+}
+
+template <int DT, int EPI>
+static hipError_t gemv_dma_epi(const ProjArgs& a, hipStream_t s) {
+  return gemv_dma_cfg<DT, EPI, SK_BK, SK_NST>(a, s);
 }
 
 template <int DT>
