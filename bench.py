@@ -40,7 +40,8 @@ def decode_bytes(s, ctx_len, act_b, kv_b) -> dict:
     w = layer_weight_elems(s) * act_b
     small = B * s.hidden * act_b * 2 + 2 * s.hidden * act_b + B * 2 * s.n_kv_heads * s.head_dim * kv_b
     gate_up = 2 * s.intermediate * s.hidden * act_b + B * (s.hidden + s.intermediate) * act_b
-    return {"total": w + kv_read + small, "weights": w, "kv_read": kv_read, "gemv_gate_up": gate_up}
+    return {"total": w + kv_read + small, "weights": w, "kv_read": kv_read, "gemv_gate_up": gate_up,
+            "attn_decode": kv_read}
 
 
 def prefill_flops(s, T) -> dict:
@@ -69,8 +70,11 @@ def cpu_baseline_decode(wl, stored, inp, budget_s: float) -> dict:
     from llama2_decoder_layer_amd import synth as S
     from oracle import llama_ref as R
     s = wl.shape
+    theta = s.rope_theta
+    if "ntk_scale" in wl.extra:
+        theta = R.ntk_rope_base(theta, wl.extra["ntk_scale"], s.head_dim)
     cfg = R.LayerConfig(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.eps,
-                        s.rope_theta)
+                        theta)
     w = R.LayerWeights(**{k: S.to_f64(v, wl.act_dtype) for k, v in stored.items()})
     B = wl.batch
     nb = B if B <= 4 else 4  # bounded sample: the first sequences of the batch
@@ -230,7 +234,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_7b_b1_ctx4096",
                     choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
-                             "stack_70b_80l"])
+                             "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -272,7 +276,11 @@ def main():
                         s.rope_theta, act, kvd, max_pos)
     rc = torch.empty(max_pos, s.head_dim // 2, dtype=torch.float32, device="cuda")
     rs = torch.empty_like(rc)
-    B.llama_rope_table(rc, rs, max_pos, s.head_dim, s.rope_theta)
+    ntk = wl.extra.get("ntk_scale")
+    if ntk is None:
+        B.llama_rope_table(rc, rs, max_pos, s.head_dim, s.rope_theta)
+    else:
+        B.llama_rope_table_ntk(rc, rs, max_pos, s.head_dim, s.rope_theta, ntk)
     sets = []
     for c in range(copies):
         w = {k: dev(v, act) for k, v in stored.items()}
@@ -290,7 +298,9 @@ def main():
         def step(i):
             lw, kc, vc = sets[i % copies]
             B.llama_layer_decode(cfg, lw, x, y, kc, vc, ctx, wl.batch, max_ctx, wl.s_max, ws)
-        dom = "gemv_gate_up"
+        # the kernel moving the most bytes: gate/up, or attention at long contexts
+        by0 = decode_bytes(s, inp["ctx_len"], act_b, kv_b)
+        dom = "attn_decode" if by0["attn_decode"] > by0["gemv_gate_up"] else "gemv_gate_up"
     else:
         x = dev(inp["x"], act)
         y = torch.empty_like(x)
@@ -364,6 +374,8 @@ def main():
                      "kv_dtype": kvd, "rotating_copies": copies}
     if decode and wl.ctx_range:
         out["config"]["ctx_len_sum"] = int(np.sum(inp["ctx_len"]))
+    if "ntk_scale" in wl.extra:
+        out["config"]["rope_ntk_scale"] = wl.extra["ntk_scale"]
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:

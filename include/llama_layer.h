@@ -147,6 +147,22 @@ int llama_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t he
                      float rope_theta, void* stream);
 
 /*
+ * NTK-aware RoPE tables for contexts beyond the trained length
+ * ("LLM架构全景解析" §3.1, position-encoding extension): the same tables as
+ * llama_rope_table with the base raised to
+ *   base' = rope_theta * ntk_scale^(head_dim / (head_dim - 2)),
+ * i.e. theta_i' = theta_i * ntk_scale^(-2i/(head_dim - 2)): the fastest pair
+ * (i = 0) keeps its frequency and the slowest (i = head_dim/2 - 1) turns
+ * ntk_scale times slower, so a context ntk_scale times longer spans the
+ * angles the slow pairs covered before.  The layer entry points take these
+ * tables unchanged.  ntk_scale = 1 gives llama_rope_table's tables.
+ * Errors: LL_ENULL, LL_EINVAL (max_pos <= 0, head_dim odd or < 4,
+ * rope_theta <= 1, ntk_scale < 1 or not finite), LL_EHIP.
+ */
+int llama_rope_table_ntk(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
+                         float rope_theta, float ntk_scale, void* stream);
+
+/*
  * Embedding lookup ("Llama2架构与推理全解析" §2.3): h[i, :] = table[ids[i], :].
  *   table [vocab, hidden] dtype; ids DEVICE int32 [n] (clamped into [0, vocab));
  *   h [n, hidden] dtype.

@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.llama_layer_decode.restype = ctypes.c_int
         L.llama_rope_table.argtypes = [P, P, I32, I32, F, P]
         L.llama_rope_table.restype = ctypes.c_int
+        L.llama_rope_table_ntk.argtypes = [P, P, I32, I32, F, F, P]
+        L.llama_rope_table_ntk.restype = ctypes.c_int
         L.llama_embed.argtypes = [P, P, P, I32, I32, I32, I32, P]
         L.llama_embed.restype = ctypes.c_int
         L.llama_head_argmax.argtypes = [P, P, P, P, P, I32, I32, I32, F, I32, P]
@@ -154,6 +156,11 @@ def llama_layer_decode(cfg, weights: LayerWeights, x, y, k_cache, v_cache, ctx_l
 def llama_rope_table(cos, sin, max_pos, head_dim, rope_theta, stream=None) -> None:
     _check(lib().llama_rope_table(_ptr(cos), _ptr(sin), max_pos, head_dim, rope_theta,
                                   _stream(stream)), "llama_rope_table")
+
+
+def llama_rope_table_ntk(cos, sin, max_pos, head_dim, rope_theta, ntk_scale, stream=None) -> None:
+    _check(lib().llama_rope_table_ntk(_ptr(cos), _ptr(sin), max_pos, head_dim, rope_theta,
+                                      ntk_scale, _stream(stream)), "llama_rope_table_ntk")
 
 
 def llama_embed(table, ids, h, n, hidden, vocab, dtype, stream=None) -> None:

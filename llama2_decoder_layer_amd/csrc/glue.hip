@@ -21,11 +21,11 @@ __global__ void rope_table_kernel(float* c, float* sn, int max_pos, int hd, doub
   }
 }
 
-hipError_t launch_rope_table(float* c, float* sn, int max_pos, int hd, float theta, hipStream_t s) {
+hipError_t launch_rope_table(float* c, float* sn, int max_pos, int hd, double theta, hipStream_t s) {
   const size_t total = (size_t)max_pos * (hd / 2);
   int grid = (int)((total + 255) / 256);
   if (grid > 4096) grid = 4096;
-  LL_LAUNCH(rope_table_kernel, dim3(grid), dim3(256), 0, s, c, sn, max_pos, hd, (double)theta);
+  LL_LAUNCH(rope_table_kernel, dim3(grid), dim3(256), 0, s, c, sn, max_pos, hd, theta);
   return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ struct AttnPrefillArgs {
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 
-hipError_t launch_rope_table(float* c, float* sn, int max_pos, int hd, float theta, hipStream_t s);
+hipError_t launch_rope_table(float* c, float* sn, int max_pos, int hd, double theta, hipStream_t s);
 hipError_t launch_embed(const void* table, const int32_t* ids, void* h, int n, int H, int vocab,
                         int dt, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int32_t* ids, int n, int vocab, hipStream_t s);

@@ -13,6 +13,7 @@
 //  * "token-wide" (prefill of > 32 tokens in bf16/f16):
 //      RMSNorm, QKV GEMM + RoPE + cache append, causal MFMA attention,
 //      O GEMM + residual, RMSNorm, gate/up GEMM + SwiGLU, down GEMM + residual.
+#include <cmath>
 #include <string.h>
 
 #include <algorithm>
@@ -450,7 +451,24 @@ int llama_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t he
   if (!cos_out || !sin_out) return LL_ENULL;
   if (max_pos <= 0 || head_dim <= 0 || head_dim % 2 || !(rope_theta > 1.f)) return LL_EINVAL;
   (void)hipGetLastError();
-  if (launch_rope_table(cos_out, sin_out, max_pos, head_dim, rope_theta, (hipStream_t)stream) != hipSuccess)
+  if (launch_rope_table(cos_out, sin_out, max_pos, head_dim, (double)rope_theta,
+                        (hipStream_t)stream) != hipSuccess)
+    return LL_EHIP;
+  return LL_OK;
+}
+
+int llama_rope_table_ntk(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
+                         float rope_theta, float ntk_scale, void* stream) {
+  if (!cos_out || !sin_out) return LL_ENULL;
+  if (max_pos <= 0 || head_dim < 4 || head_dim % 2 || !(rope_theta > 1.f) ||
+      !(ntk_scale >= 1.f) || !std::isfinite(ntk_scale))
+    return LL_EINVAL;
+  // The base grows by scale^(d/(d-2)), so theta_i = base^(-2i/d) shrinks by
+  // scale^(-2i/(d-2)): 1 for i = 0, 1/scale for i = d/2 - 1.
+  const double d = (double)head_dim;
+  const double base = (double)rope_theta * std::pow((double)ntk_scale, d / (d - 2.0));
+  (void)hipGetLastError();
+  if (launch_rope_table(cos_out, sin_out, max_pos, head_dim, base, (hipStream_t)stream) != hipSuccess)
     return LL_EHIP;
   return LL_OK;
 }

@@ -128,6 +128,11 @@ WORKLOADS = {
                                   batch=1, tokens=4096, s_max=4096),
     "decode_70b_b32_ragged": Workload("decode_70b_b32_ragged", 3, L70B, "bf16", "f16", "decode",
                                       batch=32, ctx_range=(512, 4096), s_max=4097),
+    # Long-context decode with the NTK-aware RoPE base: a 4K-trained 7B layer
+    # stretched 8x to a 32K cache.
+    "decode_7b_b1_ctx32768_ntk8": Workload("decode_7b_b1_ctx32768_ntk8", 5, L7B, "bf16", "bf16",
+                                           "decode", batch=1, ctx=32768, s_max=32769,
+                                           extra={"ntk_scale": 8.0}),
     "stack_70b_80l": Workload("stack_70b_80l", 4, L70B, "bf16", "bf16", "stack",
                               batch=1, s_max=1152, n_layers=80, vocab=32000, prompt=1024,
                               new_tokens=128),

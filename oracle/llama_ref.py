@@ -118,6 +118,17 @@ def rope_inv_freq(head_dim: int, rope_theta: float) -> np.ndarray:
     return np.power(F64(rope_theta), -2.0 * i / head_dim)
 
 
+def ntk_rope_base(rope_theta: float, ntk_scale: float, head_dim: int) -> float:
+    """RoPE base for a context ntk_scale times the trained one, by the
+    NTK-aware rule of "LLM架构全景解析" §3.1 (position-encoding extension): the
+    base is multiplied by ntk_scale^(dim/(dim-2)), dim being the rotated
+    dimension of a head.  With this base, rope() and every layer function
+    apply the extended encoding unchanged.
+    """
+    d = F64(head_dim)
+    return F64(rope_theta) * np.power(F64(ntk_scale), d / (d - 2.0))
+
+
 def rope(z: np.ndarray, positions: np.ndarray, rope_theta: float) -> np.ndarray:
     """Rotate adjacent pairs (2i, 2i+1) of every head by angle m * theta_i.
 

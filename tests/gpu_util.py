@@ -40,9 +40,12 @@ def rel_err(got, want) -> float:
     return float(np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30))
 
 
-def oracle_cfg(shape: S.Shape) -> R.LayerConfig:
+def oracle_cfg(shape: S.Shape, ntk_scale=None) -> R.LayerConfig:
+    theta = shape.rope_theta
+    if ntk_scale is not None:
+        theta = R.ntk_rope_base(theta, ntk_scale, shape.head_dim)
     return R.LayerConfig(shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim,
-                         shape.intermediate, shape.eps, shape.rope_theta)
+                         shape.intermediate, shape.eps, theta)
 
 
 def oracle_weights(stored: dict, dtype: str) -> R.LayerWeights:
@@ -52,14 +55,19 @@ def oracle_weights(stored: dict, dtype: str) -> R.LayerWeights:
 class DeviceLayer:
     """One layer on the device: config, weights and RoPE tables."""
 
-    def __init__(self, shape: S.Shape, stored: dict, act: str, kv: str, max_pos: int):
+    def __init__(self, shape: S.Shape, stored: dict, act: str, kv: str, max_pos: int,
+                 ntk_scale=None):
         self.shape, self.act, self.kv, self.max_pos = shape, act, kv, max_pos
         dev = {k: to_dev(v, act) for k, v in stored.items()}
         half = shape.head_dim // 2
         dev["rope_cos"] = torch.empty(max_pos, half, dtype=torch.float32, device="cuda")
         dev["rope_sin"] = torch.empty(max_pos, half, dtype=torch.float32, device="cuda")
-        B.llama_rope_table(dev["rope_cos"], dev["rope_sin"], max_pos, shape.head_dim,
-                           shape.rope_theta)
+        if ntk_scale is None:
+            B.llama_rope_table(dev["rope_cos"], dev["rope_sin"], max_pos, shape.head_dim,
+                               shape.rope_theta)
+        else:
+            B.llama_rope_table_ntk(dev["rope_cos"], dev["rope_sin"], max_pos, shape.head_dim,
+                                   shape.rope_theta, ntk_scale)
         self.cfg = B.make_config(shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                                  shape.intermediate, shape.eps, shape.rope_theta, act, kv, max_pos)
         self.weights = B.LayerWeights(dev)

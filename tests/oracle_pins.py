@@ -162,6 +162,44 @@ def check_rope_transformers():
         assert np.max(np.abs(ours[sel] - got_hf[sel])) < 1e-5
 
 
+def check_rope_ntk_scaling():
+    """NTK-aware base scaling: scale 1 is plain RoPE; the fastest pair keeps
+    its frequency and the slowest turns exactly `scale` times slower, so with
+    the pages' example (scale 8, a 4K context stretched to 32K) the slowest
+    pair's angle at position 8m equals the unscaled angle at m; every pair
+    lies between no scaling and full position interpolation."""
+    for hd in (64, 128):
+        plain = R.rope_inv_freq(hd, 10000.0)
+        assert R.ntk_rope_base(10000.0, 1.0, hd) == 10000.0
+        for scale in (2.0, 8.0, 16.0):
+            f = R.rope_inv_freq(hd, R.ntk_rope_base(10000.0, scale, hd))
+            assert f[0] == plain[0] == 1.0
+            assert abs(f[-1] * scale / plain[-1] - 1.0) < 1e-13, (hd, scale)
+            assert np.all(f <= plain * (1 + 1e-15)) and np.all(f >= plain / scale * (1 - 1e-13))
+            assert np.all(np.diff(f / plain) < 0)
+    hd, m = 128, np.array([1, 7, 512, 4095])
+    z = np.zeros((4, 1, hd))
+    z[..., -2] = 1.0  # only the slowest pair: angle = atan2 of the rotated pair
+    a_ntk = R.rope(z, 8 * m, R.ntk_rope_base(10000.0, 8.0, hd))
+    a_plain = R.rope(z, m, 10000.0)
+    assert np.max(np.abs(a_ntk - a_plain)) < 1e-12
+
+
+def check_rope_ntk_transformers():
+    """transformers' dynamic-NTK base at a sequence length where its factor
+    works out to a fixed scale: factor 2 at 4.5x the trained length gives
+    2 * 4.5 - (2 - 1) = 8."""
+    from transformers import LlamaConfig
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    hd = 128
+    cfg = LlamaConfig(hidden_size=32 * hd, num_attention_heads=32, num_key_value_heads=32,
+                      head_dim=hd, rope_theta=10000.0, max_position_embeddings=4096,
+                      rope_scaling={"rope_type": "dynamic", "factor": 2.0})
+    inv, _ = ROPE_INIT_FUNCTIONS["dynamic"](cfg, "cpu", seq_len=int(4.5 * 4096))
+    ours = R.rope_inv_freq(hd, R.ntk_rope_base(10000.0, 8.0, hd))
+    assert np.max(np.abs(inv.double().numpy() / ours - 1.0)) < 1e-6
+
+
 # --------------------------------------------------------------------------
 # Attention
 # --------------------------------------------------------------------------
@@ -463,6 +501,7 @@ def check_sizes_golden():
 ALL_CHECKS = [
     check_rmsnorm_closed_form, check_rmsnorm_scale_invariance_and_rows, check_rmsnorm_torch,
     check_rope_complex_hd2, check_rope_norm_identity_relative, check_rope_transformers,
+    check_rope_ntk_scaling, check_rope_ntk_transformers,
     check_attention_bruteforce, check_attention_invariants, check_attention_torch_sdpa,
     check_gqa_reductions, check_silu_closed_forms, check_swiglu_special_cases,
     check_layer_transformers, check_layer_cached_decode_equals_recompute,

@@ -166,6 +166,11 @@ def test_glue_validation():
     assert L.llama_rope_table(None, FAKE, 8, 64, 1e4, None) == -2
     assert L.llama_rope_table(FAKE, FAKE, 8, 63, 1e4, None) == -1
     assert L.llama_rope_table(FAKE, FAKE, 0, 64, 1e4, None) == -1
+    assert L.llama_rope_table_ntk(None, FAKE, 8, 64, 1e4, 8.0, None) == -2
+    assert L.llama_rope_table_ntk(FAKE, FAKE, 8, 2, 1e4, 8.0, None) == -1      # d - 2 = 0
+    assert L.llama_rope_table_ntk(FAKE, FAKE, 8, 64, 1e4, 0.5, None) == -1     # shrinks
+    assert L.llama_rope_table_ntk(FAKE, FAKE, 8, 64, 1e4, float("inf"), None) == -1
+    assert L.llama_rope_table_ntk(FAKE, FAKE, 8, 64, 1e4, float("nan"), None) == -1
     assert L.llama_embed(FAKE, FAKE, FAKE, 0, 256, 512, 1, None) == -1
     assert L.llama_embed(FAKE, FAKE + 2, FAKE, 1, 256, 512, 1, None) == -3
     assert L.llama_embed(FAKE, FAKE, FAKE, 1, 256, 512, 7, None) == -1

@@ -66,24 +66,24 @@ def run_prefill_case(label, shape, act, kv, batch, tokens, start_pos, s_max, see
     return errs
 
 
-def run_decode_case(label, shape, act, kv, ctx_len, s_max, seed, x_scale=1.0):
+def run_decode_case(label, shape, act, kv, ctx_len, s_max, seed, x_scale=1.0, ntk_scale=None):
     batch = len(ctx_len)
     say(f"[{label}] decode B={batch} ctx={[int(c) for c in ctx_len][:8]} s_max={s_max} "
-        f"{act}/{kv} x*{x_scale} {shape}")
+        f"{act}/{kv} x*{x_scale} ntk={ntk_scale} {shape}")
     stored = random_layer(shape, act, seed)
     inp = S.draw_decode_inputs(np.random.SeedSequence(seed + 1), shape, batch, s_max, act, kv,
                                ctx=0)
     if x_scale != 1.0:
         inp["x"] = scale_stored(inp["x"], act, x_scale)
     ctx = np.asarray(ctx_len, dtype=np.int32)
-    dl = DeviceLayer(shape, stored, act, kv, max_pos=s_max)
+    dl = DeviceLayer(shape, stored, act, kv, max_pos=s_max, ntk_scale=ntk_scale)
     x = to_dev(inp["x"], act)
     kc = to_dev(inp["k_cache"], kv)
     vc = to_dev(inp["v_cache"], kv)
     dctx = torch.from_numpy(ctx).cuda()
     y = dl.decode(x, kc, vc, dctx, batch, int(ctx.max()), s_max)
     torch.cuda.synchronize()
-    cfg, w = oracle_cfg(shape), oracle_weights(stored, act)
+    cfg, w = oracle_cfg(shape, ntk_scale), oracle_weights(stored, act)
     x64 = S.to_f64(inp["x"], act)
     kc64 = S.to_f64(inp["k_cache"], kv)
     vc64 = S.to_f64(inp["v_cache"], kv)
@@ -149,6 +149,36 @@ def test_bf16_decode_batch_over_32():
 
 def test_f16_decode_mha():
     run_decode_case("f16-decode", S.Shape(256, 4, 4, 64, 768), "f16", "f16", [10, 129], 160, 112)
+
+
+def test_rope_table_ntk():
+    """The NTK-aware tables against the oracle's angles with the scaled base,
+    over a 32K table: within one float32 rounding of cos/sin."""
+    hd, max_pos, scale = 128, 32769, 8.0
+    c = torch.empty(max_pos, hd // 2, dtype=torch.float32, device="cuda")
+    s = torch.empty_like(c)
+    from llama2_decoder_layer_amd import binding as B
+    B.llama_rope_table_ntk(c, s, max_pos, hd, 10000.0, scale)
+    torch.cuda.synchronize()
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * \
+        R.rope_inv_freq(hd, R.ntk_rope_base(10000.0, scale, hd))[None, :]
+    ec = np.max(np.abs(c.cpu().numpy() - np.cos(ang)))
+    es = np.max(np.abs(s.cpu().numpy() - np.sin(ang)))
+    say(f"[rope-ntk] max |cos err| {ec:.2e}, |sin err| {es:.2e}")
+    assert ec < 2 ** -23 and es < 2 ** -23
+    # scale 1 gives the plain tables bit for bit
+    c1, s1 = torch.empty_like(c[:4097]), torch.empty_like(s[:4097])
+    c0, s0 = torch.empty_like(c1), torch.empty_like(s1)
+    B.llama_rope_table_ntk(c1, s1, 4097, hd, 10000.0, 1.0)
+    B.llama_rope_table(c0, s0, 4097, hd, 10000.0)
+    assert torch.equal(c1, c0) and torch.equal(s1, s0)
+
+
+def test_bf16_decode_ntk_long_context():
+    # positions past 4K with the base scaled for a 4x longer context; GQA 4:1,
+    # f16 cache, contexts spanning several attention chunks and a ragged tail
+    run_decode_case("bf16-decode-ntk4", S.Shape(512, 8, 2, 128, 1376), "bf16", "f16",
+                    [4096, 6001, 8191, 300], 8192, 114, ntk_scale=4.0)
 
 
 def test_bf16_short_prefill_skinny():
@@ -246,6 +276,35 @@ def test_decode_7b_full():
     x64 = S.to_f64(inp["x"], wl.act_dtype)
     want = R.layer_decode(oracle_cfg(wl.shape), oracle_weights(stored, wl.act_dtype), x64, kc64,
                           vc64, inp["ctx_len"])
+    got = from_dev(y)
+    p = int(inp["ctx_len"][0])
+    d_err, d_allow = delta_error(got, want, x64, wl.act_dtype)
+    errs = {"out": rel_err(got, want), "delta": d_err,
+            "k_new": rel_err(from_dev(kc)[:, :, p], kc64[:, :, p]),
+            "v_new": rel_err(from_dev(vc)[:, :, p], vc64[:, :, p])}
+    check_errors(name, errs, TOL[wl.act_dtype], {"delta": d_allow})
+
+
+def test_decode_7b_ntk8_ctx32768_full():
+    """The long-context benchmark case: a 7B layer decoding at position 32768
+    with the NTK-aware tables for an 8x context."""
+    name = "decode_7b_b1_ctx32768_ntk8"
+    wl = S.WORKLOADS[name]
+    ntk = wl.extra["ntk_scale"]
+    say(f"[{name}] drawing inputs")
+    stored, inp = S.workload_layer_and_inputs(name)
+    dl = DeviceLayer(wl.shape, stored, wl.act_dtype, wl.kv_dtype, max_pos=wl.s_max, ntk_scale=ntk)
+    x = to_dev(inp["x"], wl.act_dtype)
+    kc, vc = to_dev(inp["k_cache"], wl.kv_dtype), to_dev(inp["v_cache"], wl.kv_dtype)
+    ctx = torch.from_numpy(inp["ctx_len"]).cuda()
+    say(f"[{name}] decode on GPU")
+    y = dl.decode(x, kc, vc, ctx, wl.batch, int(inp["ctx_len"].max()), wl.s_max)
+    torch.cuda.synchronize()
+    say(f"[{name}] oracle")
+    kc64, vc64 = S.to_f64(inp["k_cache"], wl.kv_dtype), S.to_f64(inp["v_cache"], wl.kv_dtype)
+    x64 = S.to_f64(inp["x"], wl.act_dtype)
+    want = R.layer_decode(oracle_cfg(wl.shape, ntk), oracle_weights(stored, wl.act_dtype), x64,
+                          kc64, vc64, inp["ctx_len"])
     got = from_dev(y)
     p = int(inp["ctx_len"][0])
     d_err, d_allow = delta_error(got, want, x64, wl.act_dtype)

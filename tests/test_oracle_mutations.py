@@ -115,6 +115,13 @@ def _layer_generic(drop_attn_residual=False, rotate_v=False, wo_transposed=False
     return layer
 
 
+def _ntk_exponent(num_off=0.0, den_off=-2.0):
+    def base(rope_theta, ntk_scale, head_dim):
+        d = F64(head_dim)
+        return F64(rope_theta) * np.power(F64(ntk_scale), (d + num_off) / (d + den_off))
+    return base
+
+
 MUTANTS = {
     "rmsnorm_eps_outside_sqrt": ("rmsnorm", _rmsnorm_eps_outside),
     "rmsnorm_drops_gamma": ("rmsnorm", _rmsnorm_no_gamma),
@@ -122,6 +129,9 @@ MUTANTS = {
     "rope_wrong_sign": ("rope", _rope_generic(sign=-1.0)),
     "rope_half_split_pairs": ("rope", _rope_generic(half=True)),
     "rope_wrong_frequencies": ("rope", _rope_generic(freq_div=2.0)),
+    "ntk_base_scaled_linearly": ("ntk_rope_base", _ntk_exponent(den_off=0.0)),
+    "ntk_exponent_d_over_d_minus_1": ("ntk_rope_base", _ntk_exponent(den_off=-1.0)),
+    "ntk_exponent_d_over_d_plus_2": ("ntk_rope_base", _ntk_exponent(den_off=2.0)),
     "attention_no_scale": ("causal_gqa_attention", _attention_generic(scale="none")),
     "attention_scale_1_over_d": ("causal_gqa_attention", _attention_generic(scale="lin")),
     "attention_mask_excludes_self": ("causal_gqa_attention", _attention_generic(strict=True)),
