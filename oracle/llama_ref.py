@@ -41,6 +41,9 @@ Pins (tests/test_oracle_*.py, all CPU):
   layer_decode    prefill(T) then k decodes equals prefill(T + k).
   greedy/stack    argmax lowest-index tie break; cached generation equals
                   full-recompute generation.
+  sample          a hand-worked 4-token example (temperature, top-k, top-p,
+                  penalty), inverse-CDF counts over a grid of u, the greedy
+                  limits (T -> 0, top-k = 1), transformers' logits processors.
   sizes           the pages' KV-cache formula and printed sizes (tests/golden).
 No function here is "parity unpinned".
 """
@@ -292,6 +295,61 @@ def greedy(logits: np.ndarray) -> np.ndarray:
     """Pick the highest-scoring token; ties go to the lowest index
     ("Llama2架构与推理全解析" §2.5)."""
     return np.argmax(np.asarray(logits), axis=-1)
+
+
+def sampling_distribution(logits, history, temperature: float, top_k: int, top_p: float,
+                          penalty: float):
+    """The distribution one token is drawn from ("Llama2架构与推理全解析" §2.5;
+    "Llama2架构全景解析" §3 draws from softmax(logits / T)).
+
+    Steps in the pages' order: the repetition penalty lowers every token that
+    already occurred (a positive logit is divided by `penalty`, a negative
+    one multiplied, once per distinct id); the logits are divided by the
+    temperature; top-k keeps the k largest; softmax over those; top-p keeps
+    the smallest leading set, in decreasing probability, whose mass reaches
+    top_p.  Equal values are ordered by lower index first.
+
+    logits: [V]; history: ids already seen (entries < 0 ignored).
+    Returns (ids, probs): the kept tokens in that order and their
+    renormalised probabilities.
+    """
+    z = np.array(logits, dtype=F64)
+    seen = np.unique([int(t) for t in np.asarray(history).ravel() if 0 <= int(t) < z.shape[0]])
+    for t in seen:
+        z[t] = z[t] / penalty if z[t] > 0 else z[t] * penalty
+    z = z / temperature
+    order = np.lexsort((np.arange(z.shape[0]), -z))  # decreasing z, then increasing index
+    order = order[:top_k]
+    e = np.exp(z[order] - z[order[0]])
+    p = e / np.sum(e)
+    cum_before = np.concatenate(([0.0], np.cumsum(p)[:-1]))
+    keep = cum_before < top_p  # stop after the token whose mass reaches top_p
+    ids, p = order[keep], p[keep]
+    return ids, p / np.sum(p)
+
+
+def sample(logits, history, u, temperature: float, top_k: int, top_p: float,
+           penalty: float) -> np.ndarray:
+    """One token per row: draw from sampling_distribution by the inverse of its
+    cumulative distribution at the given uniform u in [0, 1) (multinomial
+    sampling with the random number passed in).  temperature 0 is the greedy
+    limit: the highest penalised logit, lowest index on ties.
+
+    logits: [n, V]; history: [n, n_hist]; u: [n].
+    """
+    logits = np.asarray(logits, dtype=F64)
+    out = np.empty(logits.shape[0], dtype=np.int64)
+    for r in range(logits.shape[0]):
+        hist = history[r] if history is not None else []
+        if temperature == 0:
+            ids, _ = sampling_distribution(logits[r], hist, 1.0, 1, 1.0, penalty)
+            out[r] = ids[0]
+            continue
+        ids, p = sampling_distribution(logits[r], hist, temperature, top_k, top_p, penalty)
+        c = np.cumsum(p)
+        i = int(np.searchsorted(c, float(u[r]), side="right"))  # first i with c[i] > u
+        out[r] = ids[min(i, len(ids) - 1)]
+    return out
 
 
 def generate_greedy(cfg: LayerConfig, layers, embed_table, final_norm, w_lm,

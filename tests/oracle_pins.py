@@ -466,6 +466,107 @@ def check_stack_cached_equals_recompute():
 # Sizes printed on the pages
 # --------------------------------------------------------------------------
 
+# --------------------------------------------------------------------------
+# Sampling
+# --------------------------------------------------------------------------
+
+def check_sampling_worked_example():
+    """Four tokens with logits log(1..4): probabilities 0.1..0.4 at T = 1,
+    worked out by hand from the definitions."""
+    l = np.log([1.0, 2.0, 3.0, 4.0])
+    ids, p = R.sampling_distribution(l, [], 1.0, 4, 1.0, 1.0)
+    assert list(ids) == [3, 2, 1, 0] and np.allclose(p, [0.4, 0.3, 0.2, 0.1], rtol=1e-14)
+    # top-k 3 renormalises over the three largest
+    ids, p = R.sampling_distribution(l, [], 1.0, 3, 1.0, 1.0)
+    assert list(ids) == [3, 2, 1] and np.allclose(p, [4 / 9, 3 / 9, 2 / 9], rtol=1e-14)
+    # top-p 0.6: 0.4 < 0.6, 0.4 + 0.3 reaches it -> two tokens, 4/7 and 3/7
+    ids, p = R.sampling_distribution(l, [], 1.0, 4, 0.6, 1.0)
+    assert list(ids) == [3, 2] and np.allclose(p, [4 / 7, 3 / 7], rtol=1e-14)
+    # top-p 0.35: the first token alone already reaches it
+    ids, _ = R.sampling_distribution(l, [], 1.0, 4, 0.35, 1.0)
+    assert list(ids) == [3]
+    # T = 2: probabilities proportional to sqrt(1..4)
+    ids, p = R.sampling_distribution(l, [], 2.0, 4, 1.0, 1.0)
+    w = np.sqrt([4.0, 3.0, 2.0, 1.0])
+    assert list(ids) == [3, 2, 1, 0] and np.allclose(p, w / w.sum(), rtol=1e-14)
+    # penalty 2 on token 3 (seen twice, penalised once): log 4 / 2 = log 2, so
+    # the weights are 1, 2, 3, 2 and the tie between tokens 1 and 3 goes to 1
+    ids, p = R.sampling_distribution(l, [3, 3, -1], 1.0, 4, 1.0, 2.0)
+    assert list(ids) == [2, 1, 3, 0] and np.allclose(p, [3 / 8, 2 / 8, 2 / 8, 1 / 8], rtol=1e-14)
+    # a negative logit is multiplied: logits (-1, 0) with token 0 penalised by 3
+    ids, p = R.sampling_distribution(np.array([-1.0, 0.0]), [0], 1.0, 2, 1.0, 3.0)
+    assert list(ids) == [1, 0] and np.isclose(p[1] / p[0], np.exp(-3.0), rtol=1e-14)
+    # inverse CDF over (0.4, 0.7, 0.9, 1.0)
+    for u, want in ((0.0, 3), (0.39, 3), (0.41, 2), (0.69, 2), (0.71, 1), (0.95, 0), (0.999, 0)):
+        assert R.sample(l[None], [[]], [u], 1.0, 4, 1.0, 1.0)[0] == want, u
+
+
+def check_sampling_inverse_cdf_counts():
+    """Over a grid of N evenly spaced u, every kept token is drawn N * p times
+    to within one, and no other token is drawn."""
+    r = _rng(21)
+    V, N = 300, 20000
+    logits = r.standard_normal(V) * 2.0
+    hist = r.integers(0, V, 40)
+    ids, p = R.sampling_distribution(logits, hist, 0.8, 120, 0.85, 1.3)
+    u = (np.arange(N) + 0.5) / N
+    got = R.sample(np.repeat(logits[None], N, 0), np.repeat(hist[None], N, 0), u, 0.8, 120, 0.85,
+                   1.3)
+    counts = np.bincount(got, minlength=V)
+    assert np.all(np.abs(counts[ids] - N * p) <= 1.0 + 1e-9)
+    assert counts.sum() == counts[ids].sum() == N
+    assert abs(np.sum(p) - 1.0) < 1e-12 and len(ids) <= 120
+
+
+def check_sampling_greedy_limits():
+    """T = 0, top-k = 1 and a vanishing temperature all pick the highest
+    penalised logit; ties go to the lowest index."""
+    r = _rng(22)
+    for _ in range(20):
+        V = int(r.integers(2, 500))
+        l = r.standard_normal(V)
+        hist = r.integers(0, V, 5)
+        pen = np.array(l)
+        for t in np.unique(hist):
+            pen[t] = pen[t] / 1.2 if pen[t] > 0 else pen[t] * 1.2
+        want = int(np.argmax(pen))
+        u = [float(r.random())]
+        assert R.sample(l[None], [hist], u, 0.0, 50, 0.9, 1.2)[0] == want
+        assert R.sample(l[None], [hist], u, 1.0, 1, 0.9, 1.2)[0] == want
+        top2 = np.sort(pen)[-2:]
+        if top2[1] - top2[0] > 1e-3:
+            assert R.sample(l[None], [hist], u, 1e-6, V, 1.0, 1.2)[0] == want
+    tie = np.array([0.5, 2.0, 2.0, 1.0])
+    assert R.sample(tie[None], [[]], [0.9], 0.0, 4, 1.0, 1.0)[0] == 1
+    assert R.sample(tie[None], [[]], [0.9], 1.0, 1, 1.0, 1.0)[0] == 1
+
+
+def check_sampling_transformers():
+    """transformers' repetition-penalty, temperature, top-k and top-p
+    processors, applied in the same order, keep the same tokens with the same
+    probabilities."""
+    from transformers.generation.logits_process import (RepetitionPenaltyLogitsProcessor,
+                                                        TemperatureLogitsWarper,
+                                                        TopKLogitsWarper, TopPLogitsWarper)
+    r = _rng(23)
+    for T, k, tp, pen in ((0.7, 50, 0.9, 1.1), (1.0, 300, 0.5, 1.5), (0.3, 8, 1.0, 1.0)):
+        V = 1000
+        l = r.standard_normal(V) * 3.0
+        hist = r.integers(0, V, 64)
+        ids, p = R.sampling_distribution(l, hist, T, k, tp, pen)
+        x = torch.from_numpy(l)[None]
+        h = torch.from_numpy(hist)[None]
+        x = RepetitionPenaltyLogitsProcessor(pen)(h, x)
+        x = TemperatureLogitsWarper(T)(h, x)
+        x = TopKLogitsWarper(k)(h, x)
+        if tp < 1.0:
+            x = TopPLogitsWarper(tp)(h, x)
+        q = torch.softmax(x, -1)[0].numpy()
+        kept = np.nonzero(q)[0]
+        assert set(kept) == set(ids), (T, k, tp, pen)
+        assert np.max(np.abs(q[ids] - p)) < 1e-12
+
+
 def load_golden(name):
     with open(os.path.join(GOLDEN, name)) as f:
         return json.load(f)
@@ -506,5 +607,6 @@ ALL_CHECKS = [
     check_gqa_reductions, check_silu_closed_forms, check_swiglu_special_cases,
     check_layer_transformers, check_layer_cached_decode_equals_recompute,
     check_layer_ragged_batch, check_greedy_ties, check_stack_cached_equals_recompute,
-    check_sizes_golden,
+    check_sizes_golden, check_sampling_worked_example, check_sampling_inverse_cdf_counts,
+    check_sampling_greedy_limits, check_sampling_transformers,
 ]

@@ -122,6 +122,42 @@ def _ntk_exponent(num_off=0.0, den_off=-2.0):
     return base
 
 
+def _sampling_generic(pen_inverted=False, pen_per_occurrence=False, temp_mul=False,
+                      top_p_exclusive=False, top_k_extra=0):
+    def dist(logits, history, temperature, top_k, top_p, penalty):
+        z = np.array(logits, dtype=F64)
+        hist = [int(t) for t in np.asarray(history).ravel() if 0 <= int(t) < z.shape[0]]
+        for t in (hist if pen_per_occurrence else np.unique(hist)):
+            if pen_inverted:
+                z[t] = z[t] * penalty if z[t] > 0 else z[t] / penalty
+            else:
+                z[t] = z[t] / penalty if z[t] > 0 else z[t] * penalty
+        z = z * temperature if temp_mul else z / temperature
+        order = np.lexsort((np.arange(z.shape[0]), -z))[:top_k + top_k_extra]
+        e = np.exp(z[order] - z[order[0]])
+        p = e / np.sum(e)
+        if top_p_exclusive:
+            keep = np.cumsum(p) < top_p
+            keep[0] = True
+        else:
+            keep = np.concatenate(([0.0], np.cumsum(p)[:-1])) < top_p
+        return order[keep], p[keep] / np.sum(p[keep])
+    return dist
+
+
+def _sample_index_order(logits, history, u, temperature, top_k, top_p, penalty):
+    logits = np.asarray(logits, dtype=F64)
+    out = np.empty(logits.shape[0], dtype=np.int64)
+    for r in range(logits.shape[0]):
+        ids, p = R.sampling_distribution(logits[r], history[r] if history is not None else [],
+                                         temperature if temperature else 1.0,
+                                         top_k if temperature else 1, top_p, penalty)
+        o = np.argsort(ids)  # walks the kept tokens by index instead of by probability
+        i = int(np.searchsorted(np.cumsum(p[o]), float(u[r]), side="right"))
+        out[r] = ids[o][min(i, len(ids) - 1)]
+    return out
+
+
 MUTANTS = {
     "rmsnorm_eps_outside_sqrt": ("rmsnorm", _rmsnorm_eps_outside),
     "rmsnorm_drops_gamma": ("rmsnorm", _rmsnorm_no_gamma),
@@ -132,6 +168,14 @@ MUTANTS = {
     "ntk_base_scaled_linearly": ("ntk_rope_base", _ntk_exponent(den_off=0.0)),
     "ntk_exponent_d_over_d_minus_1": ("ntk_rope_base", _ntk_exponent(den_off=-1.0)),
     "ntk_exponent_d_over_d_plus_2": ("ntk_rope_base", _ntk_exponent(den_off=2.0)),
+    "sampling_penalty_inverted": ("sampling_distribution", _sampling_generic(pen_inverted=True)),
+    "sampling_penalty_per_occurrence": ("sampling_distribution",
+                                        _sampling_generic(pen_per_occurrence=True)),
+    "sampling_temperature_multiplies": ("sampling_distribution", _sampling_generic(temp_mul=True)),
+    "sampling_top_p_drops_crossing_token": ("sampling_distribution",
+                                            _sampling_generic(top_p_exclusive=True)),
+    "sampling_top_k_off_by_one": ("sampling_distribution", _sampling_generic(top_k_extra=1)),
+    "sampling_walks_index_order": ("sample", _sample_index_order),
     "attention_no_scale": ("causal_gqa_attention", _attention_generic(scale="none")),
     "attention_scale_1_over_d": ("causal_gqa_attention", _attention_generic(scale="lin")),
     "attention_mask_excludes_self": ("causal_gqa_attention", _attention_generic(strict=True)),
