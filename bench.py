@@ -227,6 +227,77 @@ def bench_stack(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def bench_sample(args, wl):
+    """Sampling after the LM head: one step = one llama_sample call over the
+    batch.  The logits come straight from the LM head in a real step, so one
+    resident copy is timed (it is 4 MB)."""
+    import torch
+    from llama2_decoder_layer_amd import binding as B
+    from llama2_decoder_layer_amd import synth as S
+    e = wl.extra
+    inp = S.draw_sample_inputs(wl.name)
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    hist = torch.from_numpy(inp["history"]).cuda()
+    u = torch.from_numpy(inp["u"]).cuda()
+    ids = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
+
+    def step():
+        B.llama_sample(logits, hist, u, ids, e["temperature"], e["top_k"], e["top_p"], e["penalty"])
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kid = B.kernel_id("sample")
+    B.llama_layer_timer_start(kid, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kms, kn = B.llama_layer_timer_stop()
+    ms_step = el * 1e3 / args.steps
+    kavg_s = kms / 1e3 / max(kn, 1)
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    nbytes = wl.batch * (wl.vocab * 4 + e["n_hist"] * 4 + 4 + 4)
+    from llama2_decoder_layer_amd.profiling import load_traffic
+    tr = load_traffic("sample", wl.name)
+    ach = nbytes / kavg_s / 1e9
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded; see synth.py)",
+           "value": wl.batch / (ms_step / 1e3), "unit": "tokens/s",
+           "roofline": {"bound": "hbm", "kernel": "sample", "achieved": ach,
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                        "traffic": None if tr is None else tr["bytes"],
+                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": kavg_s * 1e6,
+                        "launches_timed": kn},
+           "config": {"workload": wl.name, "batch": wl.batch, "vocab": wl.vocab, **e}}
+    if args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    else:
+        from oracle import llama_ref as R
+        lg = inp["logits"].astype(np.float64)
+        u64 = inp["u"].astype(np.float64)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            R.sample(lg, inp["history"], u64, e["temperature"], e["top_k"], e["top_p"],
+                     e["penalty"])
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget:
+                break
+        out["cpu_baseline"] = {"value": n * wl.batch / el, "unit": "tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{n} oracle calls over the {wl.batch} rows in {el:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,7 +305,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_7b_b1_ctx4096",
                     choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
-                             "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8"])
+                             "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8",
+                             "sample_b32_v32000"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -255,6 +327,9 @@ def main():
     wl = S.WORKLOADS[args.workload]
     if wl.phase == "stack":
         bench_stack(args, wl)
+        return
+    if wl.phase == "sample":
+        bench_sample(args, wl)
         return
     s = wl.shape
     act, kvd = wl.act_dtype, wl.kv_dtype

@@ -184,6 +184,36 @@ int llama_head_argmax(const void* final_norm, const void* w_lm, const void* h,
                       int32_t* ids_out, float* logits, int32_t n, int32_t hidden,
                       int32_t vocab, float eps, int32_t dtype, void* stream);
 
+/*
+ * Token sampling after the LM head ("Llama2架构与推理全解析" §2.5 for the
+ * steps, §3.3 for typical settings -- temperature 0.7, top-p 0.9, top-k 50,
+ * repetition penalty 1.1; "Llama2架构全景解析" §3 draws from
+ * softmax(logits / T)).  For each row r:
+ *   1. every distinct id of history[r] lowers its logit: divided by
+ *      `penalty` if positive, multiplied by it otherwise (penalty 1: off);
+ *   2. z = logit / temperature;
+ *   3. top-k keeps the top_k largest z (equal z: lower index first);
+ *   4. p = softmax over those;
+ *   5. top-p keeps the smallest leading set, in that order, whose mass
+ *      reaches top_p (top_p 1: all);
+ *   6. ids_out[r] = the first kept token whose cumulative mass exceeds
+ *      u[r] times the kept mass (inverse-CDF draw at the caller's uniform).
+ * temperature 0 is the greedy limit: the highest penalised logit, lowest
+ * index on ties.  Mass sums run in float32.
+ *   logits   DEVICE float32 [n, vocab], 4-byte aligned
+ *   history  DEVICE int32 [n, n_hist]; ids outside [0, vocab) (e.g. -1
+ *            padding) are ignored; may be NULL when n_hist == 0
+ *   u        DEVICE float32 [n], uniforms in [0, 1)
+ *   ids_out  DEVICE int32 [n]
+ * One workgroup per row; nothing is allocated.  n == 0 does nothing.
+ * Errors: LL_ENULL, LL_EALIGN, LL_EINVAL (vocab not in [1, 32768], top_k not
+ * in [1, 1024], top_p not in (0, 1], temperature < 0 or not finite,
+ * penalty <= 0 or not finite, n < 0, n_hist < 0), LL_EHIP.
+ */
+int llama_sample(const float* logits, const int32_t* history, int32_t n_hist, const float* u,
+                 int32_t* ids_out, int32_t n, int32_t vocab, float temperature, int32_t top_k,
+                 float top_p, float penalty, void* stream);
+
 /* Static description of an error code. */
 const char* llama_layer_strerror(int code);
 

@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.llama_rope_table.restype = ctypes.c_int
         L.llama_rope_table_ntk.argtypes = [P, P, I32, I32, F, F, P]
         L.llama_rope_table_ntk.restype = ctypes.c_int
+        L.llama_sample.argtypes = [P, P, I32, P, P, I32, I32, F, I32, F, F, P]
+        L.llama_sample.restype = ctypes.c_int
         L.llama_embed.argtypes = [P, P, P, I32, I32, I32, I32, P]
         L.llama_embed.restype = ctypes.c_int
         L.llama_head_argmax.argtypes = [P, P, P, P, P, I32, I32, I32, F, I32, P]
@@ -156,6 +158,17 @@ def llama_layer_decode(cfg, weights: LayerWeights, x, y, k_cache, v_cache, ctx_l
 def llama_rope_table(cos, sin, max_pos, head_dim, rope_theta, stream=None) -> None:
     _check(lib().llama_rope_table(_ptr(cos), _ptr(sin), max_pos, head_dim, rope_theta,
                                   _stream(stream)), "llama_rope_table")
+
+
+def llama_sample(logits, history, u, ids_out, temperature, top_k, top_p, penalty,
+                 stream=None) -> None:
+    """logits [n, vocab] float32, history [n, n_hist] int32 or None, u [n]
+    float32, ids_out [n] int32; all device tensors."""
+    n, vocab = logits.shape
+    n_hist = 0 if history is None else history.shape[1]
+    _check(lib().llama_sample(_ptr(logits), _ptr(history) if n_hist else None, n_hist, _ptr(u),
+                              _ptr(ids_out), n, vocab, temperature, top_k, top_p, penalty,
+                              _stream(stream)), "llama_sample")
 
 
 def llama_rope_table_ntk(cos, sin, max_pos, head_dim, rope_theta, ntk_scale, stream=None) -> None:

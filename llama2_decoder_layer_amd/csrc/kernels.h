@@ -119,6 +119,7 @@ enum KernelId {
   KID_GEMM_DOWN,
   KID_ATTN_DECODE,
   KID_ATTN_PREFILL,
+  KID_SAMPLE,
   KID_COUNT
 };
 // Benchmark timer.  timer_before arms an event pair for the next launch when
@@ -134,6 +135,21 @@ void timer_after(int kid, hipStream_t s);
 ArmedEvents take_armed_events();
 
 // Every kernel of the library is launched through this macro.
+// Token sampling, one workgroup per row (vocab <= SAMPLE_MAX_VOCAB, top_k <= 1024).
+constexpr int SAMPLE_MAX_VOCAB = 32768;
+struct SampleArgs {
+  const float* logits;     // [n, vocab]
+  const int32_t* history;  // [n, n_hist] or nullptr
+  int n_hist;
+  const float* u;          // [n]
+  int32_t* ids_out;        // [n]
+  int n, vocab;
+  float temperature;       // 0: greedy
+  int top_k;
+  float top_p, penalty;
+};
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+
 #define LL_LAUNCH(kernel, grid, block, shm, stream, ...)                                      \
   do {                                                                                        \
     const ::ll::ArmedEvents ev_ = ::ll::take_armed_events();                                  \

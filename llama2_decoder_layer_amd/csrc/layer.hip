@@ -33,7 +33,8 @@ static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 static const char* kernel_names[KID_COUNT] = {
     "rmsnorm",        "gemv_qkv",    "gemv_o",    "gemv_gate_up",   "gemv_down",  "gemm_qkv",
-    "gemm_o",         "gemm_gate_up", "gemm_down", "attn_decode",   "attn_prefill"};
+    "gemm_o",         "gemm_gate_up", "gemm_down", "attn_decode",   "attn_prefill",
+    "sample"};
 
 struct Timer {
   int kid = -1;
@@ -514,6 +515,37 @@ int llama_head_argmax(const void* final_norm, const void* w_lm, const void* h, i
   }
   if (launch_argmax(logits, ids_out, n, vocab, s) != hipSuccess) return LL_EHIP;
   return LL_OK;
+}
+
+int llama_sample(const float* logits, const int32_t* history, int32_t n_hist, const float* u,
+                 int32_t* ids_out, int32_t n, int32_t vocab, float temperature, int32_t top_k,
+                 float top_p, float penalty, void* stream) {
+  int rc = check_ptrs4({logits, u, ids_out});
+  if (rc) return rc;
+  if (n_hist < 0 || n < 0) return LL_EINVAL;
+  if (n_hist > 0 && (rc = check_ptrs4({history}))) return rc;
+  if (vocab < 1 || vocab > SAMPLE_MAX_VOCAB || top_k < 1 || top_k > 1024 || !(top_p > 0.f && top_p <= 1.f) ||
+      !(temperature >= 0.f) || !std::isfinite(temperature) || !(penalty > 0.f) ||
+      !std::isfinite(penalty))
+    return LL_EINVAL;
+  if (n == 0) return LL_OK;
+  SampleArgs a;
+  a.logits = logits;
+  a.history = n_hist > 0 ? history : nullptr;
+  a.n_hist = n_hist;
+  a.u = u;
+  a.ids_out = ids_out;
+  a.n = n;
+  a.vocab = vocab;
+  a.temperature = temperature;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.penalty = penalty;
+  (void)hipGetLastError();
+  timer_before(KID_SAMPLE, (hipStream_t)stream);
+  const hipError_t e = launch_sample(a, (hipStream_t)stream);
+  timer_after(KID_SAMPLE, (hipStream_t)stream);
+  return e == hipSuccess ? LL_OK : LL_EHIP;
 }
 
 const char* llama_layer_strerror(int code) {

@@ -44,6 +44,7 @@ KERNELS = {
     "gemm_qkv": (r"gemm_(dma_)?kernel<\d+, 0,", ["gemm.hip"] + _COMMON),
     "attn_prefill": (r"attn_prefill(_tr)?_kernel<", ["attn_prefill.hip"] + _COMMON),
     "attn_decode": (r"attn_(split|gqa)_kernel<", ["attn_decode.hip"] + _COMMON),
+    "sample": (r"sample_kernel<", ["sample.hip"] + _COMMON),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 NOTE = "(REPO is the repository root, OUT the output directory.)"

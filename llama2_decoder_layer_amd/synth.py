@@ -133,6 +133,12 @@ WORKLOADS = {
     "decode_7b_b1_ctx32768_ntk8": Workload("decode_7b_b1_ctx32768_ntk8", 5, L7B, "bf16", "bf16",
                                            "decode", batch=1, ctx=32768, s_max=32769,
                                            extra={"ntk_scale": 8.0}),
+    # Sampling after the LM head: 32 rows of a 32000-token vocabulary with the
+    # pages' dialogue settings and 256 previous ids per row.
+    "sample_b32_v32000": Workload("sample_b32_v32000", 6, L70B, "f32", "f32", "sample",
+                                  batch=32, vocab=32000,
+                                  extra={"temperature": 0.7, "top_k": 50, "top_p": 0.9,
+                                         "penalty": 1.1, "n_hist": 256}),
     "stack_70b_80l": Workload("stack_70b_80l", 4, L70B, "bf16", "bf16", "stack",
                               batch=1, s_max=1152, n_layers=80, vocab=32000, prompt=1024,
                               new_tokens=128),
@@ -297,6 +303,18 @@ def draw_prefill_inputs(ss: np.random.SeedSequence, s: Shape, batch: int, tokens
         kc[:, :, :start_pos] = normal(k_k, pshape, 1.0, kv_dtype)
         vc[:, :, :start_pos] = normal(k_v, pshape, 1.0, kv_dtype)
     return dict(x=x, k_cache=kc, v_cache=vc, start_pos=start_pos)
+
+
+def draw_sample_inputs(name: str) -> dict:
+    """Logits [B, V] ~ 3 N(0, 1) in float32, previous ids U{0..V-1} and the
+    uniforms the draw consumes, for a sampling workload."""
+    w = WORKLOADS[name]
+    k_l, k_h, k_u = inputs_seed(w.index).spawn(3)
+    logits = normal(k_l, (w.batch, w.vocab), 3.0, "f32")
+    hist = np.random.Generator(np.random.PCG64(k_h)).integers(
+        0, w.vocab, (w.batch, w.extra["n_hist"]), dtype=np.int64).astype(np.int32)
+    u = np.random.Generator(np.random.PCG64(k_u)).random(w.batch).astype(np.float32)
+    return dict(logits=np.asarray(logits, np.float32), history=hist, u=u)
 
 
 def workload_layer_and_inputs(name: str) -> tuple:

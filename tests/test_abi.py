@@ -49,7 +49,8 @@ def test_kernel_names():
     while B.llama_layer_kernel_name(i) is not None:
         names.append(B.llama_layer_kernel_name(i))
         i += 1
-    assert {"gemv_qkv", "gemv_gate_up", "gemm_qkv", "attn_decode", "attn_prefill"} <= set(names)
+    assert {"gemv_qkv", "gemv_gate_up", "gemm_qkv", "attn_decode", "attn_prefill",
+            "sample"} <= set(names)
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call here fails validation first
@@ -171,6 +172,21 @@ def test_glue_validation():
     assert L.llama_rope_table_ntk(FAKE, FAKE, 8, 64, 1e4, 0.5, None) == -1     # shrinks
     assert L.llama_rope_table_ntk(FAKE, FAKE, 8, 64, 1e4, float("inf"), None) == -1
     assert L.llama_rope_table_ntk(FAKE, FAKE, 8, 64, 1e4, float("nan"), None) == -1
+    # llama_sample: logits, history, n_hist, u, ids, n, vocab, T, top_k, top_p, penalty
+    S = L.llama_sample
+    assert S(None, None, 0, FAKE, FAKE, 4, 32000, 0.7, 50, 0.9, 1.1, None) == -2
+    assert S(FAKE, None, 3, FAKE, FAKE, 4, 32000, 0.7, 50, 0.9, 1.1, None) == -2  # history needed
+    assert S(FAKE + 2, None, 0, FAKE, FAKE, 4, 32000, 0.7, 50, 0.9, 1.1, None) == -3
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32769, 0.7, 50, 0.9, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, 0.7, 1025, 0.9, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, 0.7, 0, 0.9, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, 0.7, 50, 0.0, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, 0.7, 50, 1.5, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, -0.1, 50, 0.9, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, float("inf"), 50, 0.9, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, 0.7, 50, 0.9, 0.0, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, -1, 32000, 0.7, 50, 0.9, 1.1, None) == -1
+    assert S(FAKE, None, 0, FAKE, FAKE, 0, 32000, 0.7, 50, 0.9, 1.1, None) == 0  # empty: no launch
     assert L.llama_embed(FAKE, FAKE, FAKE, 0, 256, 512, 1, None) == -1
     assert L.llama_embed(FAKE, FAKE + 2, FAKE, 1, 256, 512, 1, None) == -3
     assert L.llama_embed(FAKE, FAKE, FAKE, 1, 256, 512, 7, None) == -1
