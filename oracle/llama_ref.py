@@ -41,6 +41,9 @@ Pins (tests/test_oracle_*.py, all CPU):
   layer_decode    prefill(T) then k decodes equals prefill(T + k).
   greedy/stack    argmax lowest-index tie break; cached generation equals
                   full-recompute generation.
+  quantize_w8     the round-to-nearest bound |w - q s| <= s/2, the largest
+                  magnitude on +-127, sign symmetry, exact re-quantisation of
+                  dequantised rows, zero rows.
   sample          a hand-worked 4-token example (temperature, top-k, top-p,
                   penalty), inverse-CDF counts over a grid of u, the greedy
                   limits (T -> 0, top-k = 1), transformers' logits processors.
@@ -295,6 +298,34 @@ def greedy(logits: np.ndarray) -> np.ndarray:
     """Pick the highest-scoring token; ties go to the lowest index
     ("Llama2架构与推理全解析" §2.5)."""
     return np.argmax(np.asarray(logits), axis=-1)
+
+
+def quantize_w8_rows(w):
+    """Weight-only INT8 by rows ("Llama2架构与推理全解析" §3.2: one byte per
+    weight instead of two, with a small loss of precision).
+
+    Reading: symmetric round-to-nearest per output row, the scale being the
+    row's largest magnitude over 127; codes = rint(w / scale) clipped to
+    [-127, 127] (ties to even), an all-zero row gets scale 0 and codes 0.  The
+    scale and the division are taken in float32, the precision of the kernel,
+    so that both sides pick the same integer codes.
+
+    w: [rows, cols] (values exactly representable in float32).
+    Returns (codes int8 [rows, cols], scales float32 [rows]).
+    """
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint(w32 / safe[:, None])
+    q = np.where(scale[:, None] > 0, np.clip(q, -127, 127), 0)
+    return q.astype(np.int8), scale
+
+
+def dequantize_w8(codes, scales) -> np.ndarray:
+    """The weights an INT8 layer computes with: codes times the row scale, in
+    float64 (exact: an 8-bit integer times a float32 scale)."""
+    return np.asarray(codes, dtype=F64) * np.asarray(scales, dtype=F64)[:, None]
 
 
 def sampling_distribution(logits, history, temperature: float, top_k: int, top_p: float,

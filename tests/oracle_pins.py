@@ -467,6 +467,40 @@ def check_stack_cached_equals_recompute():
 # --------------------------------------------------------------------------
 
 # --------------------------------------------------------------------------
+# Weight-only INT8
+# --------------------------------------------------------------------------
+
+def check_quantize_w8():
+    """Round to nearest per row: every weight within half a step of its code
+    times the scale, each row's largest magnitude on +-127, codes of -w are
+    minus the codes of w, dequantised rows quantise back to themselves, a
+    zero row stays zero, and a hand-worked row."""
+    r = _rng(30)
+    w = (r.standard_normal((64, 300)) * 0.02).astype(np.float32)
+    w[5] = 0.0
+    w[7, :] = 0.0
+    w[7, 3] = -0.5
+    q, sc = R.quantize_w8_rows(w)
+    assert q.dtype == np.int8 and sc.dtype == np.float32
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    err = np.abs(w.astype(np.float64) - R.dequantize_w8(q, sc))
+    assert np.all(err <= sc.astype(np.float64)[:, None] * (0.5 + 1e-6))
+    nz = sc > 0
+    assert np.all(np.max(np.abs(q[nz].astype(int)), axis=1) == 127)
+    assert sc[5] == 0 and not np.any(q[5])
+    assert q[7, 3] == -127 and np.count_nonzero(q[7]) == 1
+    qn, scn = R.quantize_w8_rows(-w)
+    assert np.array_equal(qn, -q) and np.array_equal(scn, sc)
+    back = R.dequantize_w8(q, sc).astype(np.float32)
+    q2, sc2 = R.quantize_w8_rows(back)
+    assert np.array_equal(q2, q) and np.allclose(sc2, sc, rtol=1e-6, atol=0)
+    # by hand: max 1.27 -> scale 0.01; -0.64 -> -64, 0.015 -> 1.5 (just above
+    # in float32) -> 2, 0.0051 -> 0.51 -> 1
+    q, sc = R.quantize_w8_rows(np.array([[1.27, -0.64, 0.015, 0.0051, -1.27]], np.float32))
+    assert abs(sc[0] - 0.01) < 1e-9 and list(q[0]) == [127, -64, 2, 1, -127]
+
+
+# --------------------------------------------------------------------------
 # Sampling
 # --------------------------------------------------------------------------
 
@@ -607,6 +641,6 @@ ALL_CHECKS = [
     check_gqa_reductions, check_silu_closed_forms, check_swiglu_special_cases,
     check_layer_transformers, check_layer_cached_decode_equals_recompute,
     check_layer_ragged_batch, check_greedy_ties, check_stack_cached_equals_recompute,
-    check_sizes_golden, check_sampling_worked_example, check_sampling_inverse_cdf_counts,
+    check_sizes_golden, check_quantize_w8, check_sampling_worked_example, check_sampling_inverse_cdf_counts,
     check_sampling_greedy_limits, check_sampling_transformers,
 ]
