@@ -32,14 +32,21 @@ def layer_weight_elems(s) -> int:
     return (nh + 2 * nkv) * hd * H + H * nh * hd + 2 * I * H + H * I
 
 
-def decode_bytes(s, ctx_len, act_b, kv_b) -> dict:
-    """Algorithmic HBM bytes of one decode call: each weight once, each cached
-    K/V entry that is attended once, the new K/V entries, x, y and the gains."""
+def decode_bytes(s, ctx_len, act_b, kv_b, w8=False) -> dict:
+    """Algorithmic HBM bytes of one decode call: each weight once (INT8: one
+    byte per weight and a float32 scale per row), each cached K/V entry that is
+    attended once, the new K/V entries, x, y and the gains."""
     B = len(ctx_len)
     kv_read = int(np.sum(np.asarray(ctx_len, np.int64) + 1)) * s.n_kv_heads * s.head_dim * 2 * kv_b
-    w = layer_weight_elems(s) * act_b
+    if w8:
+        rows = (s.n_heads + 2 * s.n_kv_heads) * s.head_dim + s.hidden + 2 * s.intermediate + s.hidden
+        w = layer_weight_elems(s) + 4 * rows
+        gate_up = 2 * s.intermediate * s.hidden + 4 * 2 * s.intermediate
+    else:
+        w = layer_weight_elems(s) * act_b
+        gate_up = 2 * s.intermediate * s.hidden * act_b
     small = B * s.hidden * act_b * 2 + 2 * s.hidden * act_b + B * 2 * s.n_kv_heads * s.head_dim * kv_b
-    gate_up = 2 * s.intermediate * s.hidden * act_b + B * (s.hidden + s.intermediate) * act_b
+    gate_up += B * (s.hidden + s.intermediate) * act_b
     return {"total": w + kv_read + small, "weights": w, "kv_read": kv_read, "gemv_gate_up": gate_up,
             "attn_decode": kv_read}
 
@@ -75,7 +82,11 @@ def cpu_baseline_decode(wl, stored, inp, budget_s: float) -> dict:
         theta = R.ntk_rope_base(theta, wl.extra["ntk_scale"], s.head_dim)
     cfg = R.LayerConfig(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.eps,
                         theta)
-    w = R.LayerWeights(**{k: S.to_f64(v, wl.act_dtype) for k, v in stored.items()})
+    w = {k: S.to_f64(v, wl.act_dtype) for k, v in stored.items()}
+    if wl.extra.get("w8"):
+        for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down"):
+            w[k] = R.dequantize_w8(*R.quantize_w8_rows(w[k].astype(np.float32)))
+    w = R.LayerWeights(**w)
     B = wl.batch
     nb = B if B <= 4 else 4  # bounded sample: the first sequences of the batch
     kc = S.to_f64(inp["k_cache"][:nb], wl.kv_dtype)
@@ -306,7 +317,7 @@ def main():
     ap.add_argument("--workload", default="decode_7b_b1_ctx4096",
                     choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
                              "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8",
-                             "sample_b32_v32000"])
+                             "sample_b32_v32000", "decode_7b_b1_ctx4096_w8"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -344,7 +355,8 @@ def main():
             return torch.from_numpy(a).cuda()
         return torch.from_numpy(a.view(np.int16)).cuda().view(tdt[dt])
 
-    per_copy = layer_weight_elems(s) * act_b + 2 * inp["k_cache"].size * kv_b
+    per_copy = layer_weight_elems(s) * (1 if wl.extra.get("w8") else act_b) + \
+        2 * inp["k_cache"].size * kv_b
     copies = args.copies or max(1, min(8, -(-1_500_000_000 // per_copy)))
     max_pos = wl.s_max
     cfg = B.make_config(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.eps,
@@ -356,11 +368,23 @@ def main():
         B.llama_rope_table(rc, rs, max_pos, s.head_dim, s.rope_theta)
     else:
         B.llama_rope_table_ntk(rc, rs, max_pos, s.head_dim, s.rope_theta, ntk)
+    w8 = bool(wl.extra.get("w8"))
     sets = []
     for c in range(copies):
         w = {k: dev(v, act) for k, v in stored.items()}
         w["rope_cos"], w["rope_sin"] = rc, rs
-        sets.append((B.LayerWeights(w), dev(inp["k_cache"], kvd), dev(inp["v_cache"], kvd)))
+        if w8:
+            for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down"):
+                full = w.pop(k)
+                q = torch.empty(full.shape, dtype=torch.int8, device="cuda")
+                sc = torch.empty(full.shape[0], dtype=torch.float32, device="cuda")
+                B.llama_quantize_w8(full, q, sc, act)
+                w[k], w["s_" + k[2:]] = q, sc
+            torch.cuda.synchronize()
+            lw = B.LayerWeightsW8(w)
+        else:
+            lw = B.LayerWeights(w)
+        sets.append((lw, dev(inp["k_cache"], kvd), dev(inp["v_cache"], kvd)))
     decode = wl.phase == "decode"
     if decode:
         x = dev(inp["x"], act)
@@ -370,11 +394,13 @@ def main():
         ws = torch.empty(B.llama_layer_workspace_size(cfg, wl.batch, 1, wl.s_max), dtype=torch.uint8,
                          device="cuda")
 
+        run = B.llama_layer_decode_w8 if w8 else B.llama_layer_decode
+
         def step(i):
             lw, kc, vc = sets[i % copies]
-            B.llama_layer_decode(cfg, lw, x, y, kc, vc, ctx, wl.batch, max_ctx, wl.s_max, ws)
+            run(cfg, lw, x, y, kc, vc, ctx, wl.batch, max_ctx, wl.s_max, ws)
         # the kernel moving the most bytes: gate/up, or attention at long contexts
-        by0 = decode_bytes(s, inp["ctx_len"], act_b, kv_b)
+        by0 = decode_bytes(s, inp["ctx_len"], act_b, kv_b, w8)
         dom = "attn_decode" if by0["attn_decode"] > by0["gemv_gate_up"] else "gemv_gate_up"
     else:
         x = dev(inp["x"], act)
@@ -420,7 +446,7 @@ def main():
     tr = load_traffic(dom, wl.name)
     traffic = None if tr is None else tr["bytes"]
     if decode:
-        by = decode_bytes(s, inp["ctx_len"], act_b, kv_b)
+        by = decode_bytes(s, inp["ctx_len"], act_b, kv_b, bool(wl.extra.get("w8")))
         out.update(value=wl.batch / (ms_step / 1e3), unit="tokens/s/layer")
         layer_gbps = by["total"] / (ms_step / 1e3) / 1e9
         out["layer_hbm"] = {"bytes_per_step": by["total"], "GBps": layer_gbps,
@@ -451,6 +477,8 @@ def main():
         out["config"]["ctx_len_sum"] = int(np.sum(inp["ctx_len"]))
     if "ntk_scale" in wl.extra:
         out["config"]["rope_ntk_scale"] = wl.extra["ntk_scale"]
+    if wl.extra.get("w8"):
+        out["config"]["weights"] = "int8 codes, float32 scale per row"
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:

@@ -45,6 +45,13 @@ class ll_weights(ctypes.Structure):
                  "w_down", "rope_cos", "rope_sin")]
 
 
+class ll_weights_w8(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "w_q", "w_k", "w_v", "w_o", "ffn_norm", "w_gate", "w_up",
+                 "w_down", "s_q", "s_k", "s_v", "s_o", "s_gate", "s_up", "s_down",
+                 "rope_cos", "rope_sin")]
+
+
 _lib = None
 
 
@@ -71,6 +78,11 @@ def lib() -> ctypes.CDLL:
         L.llama_rope_table_ntk.restype = ctypes.c_int
         L.llama_sample.argtypes = [P, P, I32, P, P, I32, I32, F, I32, F, F, P]
         L.llama_sample.restype = ctypes.c_int
+        L.llama_quantize_w8.argtypes = [P, P, P, I32, I32, I32, P]
+        L.llama_quantize_w8.restype = ctypes.c_int
+        L.llama_layer_decode_w8.argtypes = [CP, ctypes.POINTER(ll_weights_w8), P, P, P, P, P,
+                                            I32, I32, I32, P, SZ, P]
+        L.llama_layer_decode_w8.restype = ctypes.c_int
         L.llama_embed.argtypes = [P, P, P, I32, I32, I32, I32, P]
         L.llama_embed.restype = ctypes.c_int
         L.llama_head_argmax.argtypes = [P, P, P, P, P, I32, I32, I32, F, I32, P]
@@ -153,6 +165,33 @@ def llama_layer_decode(cfg, weights: LayerWeights, x, y, k_cache, v_cache, ctx_l
                                   _ptr(y), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), batch,
                                   max_ctx, s_max, _ptr(ws), nbytes, _stream(stream))
     _check(rc, "llama_layer_decode")
+
+
+class LayerWeightsW8:
+    """Holds an INT8 layer's device tensors (codes, scales, norms, RoPE tables)
+    and their ll_weights_w8."""
+
+    NAMES = tuple(n for n, _ in ll_weights_w8._fields_)
+
+    def __init__(self, tensors: dict):
+        self.tensors = dict(tensors)
+        self.struct = ll_weights_w8(*[_ptr(self.tensors[n]) for n in self.NAMES])
+
+
+def llama_quantize_w8(w, q, scale, dtype, stream=None) -> None:
+    """w [rows, cols] device tensor stored in `dtype`; q int8 and scale float32 outputs."""
+    rows, cols = w.shape
+    _check(lib().llama_quantize_w8(_ptr(w), _ptr(q), _ptr(scale), rows, cols, DTYPE_CODE[dtype],
+                                   _stream(stream)), "llama_quantize_w8")
+
+
+def llama_layer_decode_w8(cfg, weights: LayerWeightsW8, x, y, k_cache, v_cache, ctx_len, batch,
+                          max_ctx, s_max, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    rc = lib().llama_layer_decode_w8(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x),
+                                     _ptr(y), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), batch,
+                                     max_ctx, s_max, _ptr(ws), nbytes, _stream(stream))
+    _check(rc, "llama_layer_decode_w8")
 
 
 def llama_rope_table(cos, sin, max_pos, head_dim, rope_theta, stream=None) -> None:

@@ -332,41 +332,71 @@ static hipError_t gemv_glb_launch(const ProjArgs& a, hipStream_t s) {
 // in LDS, and meets in LDS for the epilogue: RoPE pairs and the four
 // consecutive features of the QKV epilogue, gate and up of SwiGLU.
 // ---------------------------------------------------------------------------
-template <int DT, int EPI, bool NORM, int MT, int NWV>
+// WQ: the weights are int8 codes (16 per 16-byte load) with one float32
+// scale per row (a.wscale, by segment), applied after the reduction; the
+// activations stay in format DT.  An int8 row is half as long in bytes, so
+// each wave then streams two rows (RPW) to keep the same bytes in flight, and
+// every activation chunk read from LDS serves both.  Only single-token
+// launches with a fused norm (QKV, gate/up: many rows, and a norm pass per
+// workgroup worth spreading over more rows) do that; O and down (4096 rows at
+// 7B) keep one row per wave, or half the CUs would sit idle, and with four
+// tokens the second row's registers spill.
+template <bool WQ, int MT, bool NORM>
+constexpr int row_rows_per_wave() { return (WQ && MT == 1 && NORM) ? 2 : 1; }
+
+template <int DT, int EPI, bool NORM, int MT, int NWV, bool WQ = false>
 __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
   typedef typename Elt<DT>::T T;
+  typedef typename std::conditional<WQ, int8_t, T>::type TW;
   constexpr int E = Elt<DT>::PER16;
+  constexpr int EW = WQ ? 16 : E;          // weights per 16-byte load
+  constexpr int RPW = row_rows_per_wave<WQ, MT, NORM>();  // rows per wave
+  constexpr int NS = NWV * RPW;            // row slots per workgroup
   constexpr bool SWI = (EPI == EPI_SWIGLU);
-  constexpr int FW = SWI ? NWV / 2 : NWV;  // output features per workgroup
-  constexpr int U = 8;                                   // 1 KB chunks per batch
+  constexpr int FW = SWI ? NS / 2 : NS;    // output features per workgroup
+  // 1 KB chunks per row and batch: 8 KB a wave, except int8 for several
+  // tokens, which keeps 4 (more spill).
+  constexpr int U = (WQ && (RPW == 2 || MT > 1)) ? 4 : 8;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   T* xs = reinterpret_cast<T*>(smem);  // [M][K]
   __shared__ float rstd_s[MT];
   __shared__ float part_s[NWV];
-  __shared__ float res_s[NWV][MT];
+  __shared__ float res_s[NS][MT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int K = a.K, M = a.M;
   const int f0 = blockIdx.x * FW;
-  // This wave's row (rows past N read row 0; results dropped).
-  const T* wp;
-  {
-    const int f = f0 + (SWI ? (wave % FW) : wave);
+  // Slot s (this wave's are wave, wave + NWV, ...): feature f0 + s (SwiGLU:
+  // gate rows in the first FW slots, the matching up rows in the rest).  Rows
+  // past N read row 0; their results are dropped.  int8 rows bring a scale.
+  const TW* wp[RPW];
+  float wscale[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int slot = wave + r * NWV;
+    const int f = f0 + (SWI ? (slot % FW) : slot);
     const int fs = f < a.N ? f : 0;
-    if constexpr (SWI)
-      wp = reinterpret_cast<const T*>(wave < FW ? a.w[0] : a.w[1]) + (size_t)fs * K;
-    else
-      wp = seg_row<T>(a, fs);
+    wscale[r] = 1.f;
+    if constexpr (SWI) {
+      wp[r] = reinterpret_cast<const TW*>(slot < FW ? a.w[0] : a.w[1]) + (size_t)fs * K;
+      if constexpr (WQ) wscale[r] = a.wscale[slot < FW ? 0 : 1][fs];
+    } else {
+      wp[r] = seg_row<TW>(a, fs);
+      if constexpr (WQ)
+        wscale[r] = fs < a.seg1 ? a.wscale[0][fs]
+                  : fs < a.seg2 ? a.wscale[1][fs - a.seg1] : a.wscale[2][fs - a.seg2];
+    }
   }
-  const int nch = (K + 64 * E - 1) / (64 * E);
+  const int nch = (K + 64 * EW - 1) / (64 * EW);
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 wv[U];
+  u32x4 wv[RPW][U];
   auto load_batch = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (c0 + u) * 64 * E + lane * E;
-      wv[u] = (k < K) ? ld16_stream(wp + k) : zero;
+      const int k = (c0 + u) * 64 * EW + lane * EW;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) wv[r][u] = (k < K) ? ld16_stream(wp[r] + k) : zero;
     }
   };
   // Weight loads start before the activations are staged.
@@ -407,33 +437,58 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
   }
   __syncthreads();
 
-  float acc[MT];
+  float acc[RPW][MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
   for (int c0 = 0; c0 < nch; c0 += U) {
     if (c0 > 0) load_batch(c0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (c0 + u) * 64 * E + lane * E;
+      const int k = (c0 + u) * 64 * EW + lane * EW;
       if (k >= K) break;
-      float wf[E];
-      unpack16<DT>(wv[u], wf);
+      float wf[RPW][EW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if constexpr (WQ) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              wf[r][4 * i + b] = (float)(int8_t)(wv[r][u][i] >> (8 * b));
+        } else {
+          unpack16<DT>(wv[r][u], wf[r]);
+        }
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < M) {
-          float xf[E];
-          unpack16<DT>(ld16(xs + (size_t)m * K + k), xf);
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[m] += wf[e] * xf[e];
+          for (int h = 0; h < EW / E; ++h) {
+            float xf[E];
+            unpack16<DT>(ld16(xs + (size_t)m * K + k + h * E), xf);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+              for (int e = 0; e < E; ++e) acc[r][m] += wf[r][h * E + e] * xf[e];
+          }
         }
       }
+      // int8: keep each chunk's conversions and activation reads next to
+      // their use; hoisted across the batch they exhaust the registers.
+      if constexpr (WQ) __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = wave_sum(acc[m]);
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = wave_sum(acc[r][m]) * wscale[r];
   if (lane == 0) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) res_s[wave][m] = acc[m];
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) res_s[wave + r * NWV][m] = acc[r][m];
   }
   __syncthreads();
 
@@ -486,6 +541,58 @@ static hipError_t gemv_row_launch(const ProjArgs& a, hipStream_t s) {
   else
     LL_LAUNCH((gemv_row1_kernel<DT, EPI, NORM, 4, NWV>), dim3(grid), dim3(NWV * 64), sh, s, a);
   return hipGetLastError();
+}
+
+// int8 weights, 1-4 tokens: the row kernel with a larger activation stage.
+template <int DT, int EPI, bool NORM>
+static hipError_t gemv_row_w8_launch(const ProjArgs& a, hipStream_t s) {
+  constexpr int NWV = NORM ? 4 : 16;
+  // Features per workgroup: NWV rows (two per wave for one token), halved for
+  // SwiGLU's gate/up pairs.
+  const int rows = NWV * (a.M == 1 ? row_rows_per_wave<true, 1, NORM>()
+                                    : row_rows_per_wave<true, 4, NORM>());
+  const int FW = (EPI == EPI_SWIGLU) ? rows / 2 : rows;
+  const int grid = (a.N + FW - 1) / FW;
+  const size_t sh = gemv_lds_bytes(DT, a.M, a.K);
+  auto go = [&](auto k) -> hipError_t {
+    // Dynamic LDS beyond 64 KB has to be allowed for the kernel first.
+    if (sh > (size_t)GEMV_LDS_BYTES) {
+      const hipError_t e =
+          hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+      if (e != hipSuccess) return e;
+    }
+    LL_LAUNCH(k, dim3(grid), dim3(NWV * 64), sh, s, a);
+    return hipGetLastError();
+  };
+  if (a.M == 1) return go(gemv_row1_kernel<DT, EPI, NORM, 1, NWV, true>);
+  return go(gemv_row1_kernel<DT, EPI, NORM, 4, NWV, true>);
+}
+
+template <int DT>
+static hipError_t gemv_w8_dt(int epi, const ProjArgs& a, hipStream_t s) {
+  const bool norm = a.gamma != nullptr;
+  switch (epi) {
+    case EPI_QKV: return norm ? gemv_row_w8_launch<DT, EPI_QKV, true>(a, s)
+                              : gemv_row_w8_launch<DT, EPI_QKV, false>(a, s);
+    case EPI_RESID: return gemv_row_w8_launch<DT, EPI_RESID, false>(a, s);
+    case EPI_SWIGLU: return norm ? gemv_row_w8_launch<DT, EPI_SWIGLU, true>(a, s)
+                                 : gemv_row_w8_launch<DT, EPI_SWIGLU, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool gemv_w8_fits(int dt, int M, int K) {
+  return M >= 1 && M <= 4 && K % 16 == 0 && gemv_lds_bytes(dt, M, K) <= (size_t)GEMV_W8_LDS_BYTES;
+}
+
+hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s) {
+  if (!gemv_w8_fits(dt, a.M, a.K) || !a.wscale[0]) return hipErrorInvalidValue;
+  switch (dt) {
+    case DT_F32: return gemv_w8_dt<DT_F32>(epi, a, s);
+    case DT_BF16: return gemv_w8_dt<DT_BF16>(epi, a, s);
+    case DT_F16: return gemv_w8_dt<DT_F16>(epi, a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int DT>

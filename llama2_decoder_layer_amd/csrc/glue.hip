@@ -1,5 +1,5 @@
-// Small kernels around the layer: RoPE angle tables, embedding gather and the
-// greedy pick over logits.
+// Small kernels around the layer: RoPE angle tables, embedding gather, the
+// greedy pick over logits and the per-row int8 weight quantiser.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -75,6 +75,42 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int32_
 
 hipError_t launch_argmax(const float* logits, int32_t* ids, int n, int vocab, hipStream_t s) {
   LL_LAUNCH(argmax_kernel, dim3(n), dim3(256), 0, s, logits, ids, vocab);
+  return hipGetLastError();
+}
+
+// Weight-only int8 by rows: scale = max|w| / 127, q = rint(w / scale) in
+// [-127, 127] (a zero row: scale 0, codes 0).  One workgroup per row; the
+// division is the correctly rounded float32 one.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_w8_kernel(const void* w, int8_t* q, float* scale,
+                                                          int cols) {
+  typedef typename Elt<DT>::T T;
+  __shared__ float red[4];
+  const T* r = reinterpret_cast<const T*>(w) + (size_t)blockIdx.x * cols;
+  int8_t* qr = q + (size_t)blockIdx.x * cols;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(Elt<DT>::to_f32(r[c])));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(m, 127.0f);
+  if (threadIdx.x == 0) scale[blockIdx.x] = s;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    float v = 0.f;
+    if (s > 0.f) v = fminf(127.f, fmaxf(-127.f, rintf(__fdiv_rn(Elt<DT>::to_f32(r[c]), s))));
+    qr[c] = (int8_t)(int)v;
+  }
+}
+
+hipError_t launch_quantize_w8(int dt, const void* w, int8_t* q, float* scale, int rows, int cols,
+                              hipStream_t s) {
+  if (dt == DT_F32)
+    LL_LAUNCH(quantize_w8_kernel<DT_F32>, dim3(rows), dim3(256), 0, s, w, q, scale, cols);
+  else if (dt == DT_BF16)
+    LL_LAUNCH(quantize_w8_kernel<DT_BF16>, dim3(rows), dim3(256), 0, s, w, q, scale, cols);
+  else
+    LL_LAUNCH(quantize_w8_kernel<DT_F16>, dim3(rows), dim3(256), 0, s, w, q, scale, cols);
   return hipGetLastError();
 }
 

@@ -37,12 +37,22 @@ struct ProjArgs {
   const float* rcos;
   const float* rsin;
   float* part;        // float32 K-split partials of the streaming projection (workspace)
+  const float* wscale[3];  // int8 weights: float32 scale per row of each segment
 };
 
 // Decode-sized projection (M <= 32 tokens).  A fused norm (gamma != nullptr)
 // needs the M activation rows to fit the LDS stage: gemv_fits_lds(dt, M, K).
 hipError_t launch_gemv(int dt, int epi, const ProjArgs& a, hipStream_t s);
 bool gemv_fits_lds(int dt, int M, int K);
+// Weight-only int8 projection for 1-4 tokens (a.w int8 [N][K] per segment,
+// a.wscale float32 per row; K % 16 == 0; activations of the M tokens within
+// GEMV_W8_LDS_BYTES).
+constexpr int GEMV_W8_LDS_BYTES = 128 * 1024;
+bool gemv_w8_fits(int dt, int M, int K);
+hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
+// Per-row symmetric int8 codes and float32 scales of a [rows, cols] matrix.
+hipError_t launch_quantize_w8(int dt, const void* w, int8_t* q, float* scale, int rows, int cols,
+                              hipStream_t s);
 // Prefill projection (M tokens): MFMA tiles with fused epilogues.  When the
 // last round of 256 x 256 tiles would leave CUs idle, its tiles are split
 // along K; the partials go to a.part, which must hold gemm_partial_bytes.

@@ -192,10 +192,12 @@ static ProjArgs base_args(const ll_config* c) {
 }
 
 // Token-skinny plan for tokens [tok0, tok0 + m) of B*T.
-static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, void* y, void* kc,
-                      void* vc, const int32_t* ctx_len, int start_pos, int T, int max_ctx,
-                      int s_max, int64_t tok0, int m, uint8_t* ws, const Layout& L,
-                      hipStream_t s) {
+// With w8 set (and w unused) the projections take int8 weights and per-row
+// scales through the int8 row kernel; m is then at most 4.
+static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_w8* w8,
+                      const void* x, void* y, void* kc, void* vc, const int32_t* ctx_len,
+                      int start_pos, int T, int max_ctx, int s_max, int64_t tok0, int m,
+                      uint8_t* ws, const Layout& L, hipStream_t s) {
   const int dt = c->act_dtype;
   const size_t act = esize(dt);
   const int H = c->hidden, I = c->intermediate;
@@ -208,30 +210,42 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
 
   // RMSNorm is fused into the projection when the m activation rows fit its
   // LDS stage; otherwise a norm pass writes u first.
-  const bool fuse_norm = gemv_fits_lds(dt, m, H);
+  const bool fuse_norm = w8 ? true : gemv_fits_lds(dt, m, H);
   void* u = ws + L.u;
+  const void* attn_norm = w8 ? w8->attn_norm : w->attn_norm;
+  const void* ffn_norm = w8 ? w8->ffn_norm : w->ffn_norm;
+  auto proj = [&](int epi, const ProjArgs& pa) {
+    return w8 ? launch_gemv_w8(dt, epi, pa, s) : launch_gemv(dt, epi, pa, s);
+  };
 
   float* part = (float*)(ws + L.part);
 
   // 1. QKV + RMSNorm + RoPE + cache append.
   ProjArgs p = base_args(c);
   p.part = part;
-  p.w[0] = w->w_q; p.w[1] = w->w_k; p.w[2] = w->w_v;
+  if (w8) {
+    p.w[0] = w8->w_q; p.w[1] = w8->w_k; p.w[2] = w8->w_v;
+    p.wscale[0] = w8->s_q; p.wscale[1] = w8->s_k; p.wscale[2] = w8->s_v;
+  } else {
+    p.w[0] = w->w_q; p.w[1] = w->w_k; p.w[2] = w->w_v;
+  }
   p.seg1 = qd; p.seg2 = qd + kd;
   p.N = qd + 2 * kd; p.K = H; p.M = m; p.tok0 = (int)tok0;
   if (fuse_norm) {
-    p.x = xm; p.gamma = w->attn_norm;
+    p.x = xm; p.gamma = attn_norm;
   } else {
     timer_before(KID_RMSNORM, s);
-    LL_TRY(launch_rmsnorm(dt, xm, w->attn_norm, u, m, H, c->eps, s));
+    LL_TRY(launch_rmsnorm(dt, xm, attn_norm, u, m, H, c->eps, s));
     timer_after(KID_RMSNORM, s);
     p.x = u;
   }
   p.q32 = (float*)(ws + L.q32);
   p.kc = kc; p.vc = vc; p.ctx_len = ctx_len; p.start_pos = start_pos; p.T = T;
-  p.max_ctx = max_ctx; p.s_max = s_max; p.rcos = w->rope_cos; p.rsin = w->rope_sin;
+  p.max_ctx = max_ctx; p.s_max = s_max;
+  p.rcos = w8 ? w8->rope_cos : w->rope_cos;
+  p.rsin = w8 ? w8->rope_sin : w->rope_sin;
   timer_before(KID_GEMV_QKV, s);
-  LL_TRY(launch_gemv(dt, EPI_QKV, p, s));
+  LL_TRY(proj(EPI_QKV, p));
   timer_after(KID_GEMV_QKV, s);
 
   // 2. Attention over the cache.
@@ -272,36 +286,43 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const void* x, vo
   // 3. O projection + residual.
   ProjArgs po = base_args(c);
   po.part = part;
-  po.w[0] = w->w_o; po.seg1 = po.seg2 = H;
+  po.w[0] = w8 ? (const void*)w8->w_o : w->w_o; po.seg1 = po.seg2 = H;
+  if (w8) po.wscale[0] = w8->s_o;
   po.N = H; po.K = qd; po.M = m; po.x = o; po.resid = xm; po.y = h1;
   timer_before(KID_GEMV_O, s);
-  LL_TRY(launch_gemv(dt, EPI_RESID, po, s));
+  LL_TRY(proj(EPI_RESID, po));
   timer_after(KID_GEMV_O, s);
 
   // 4. gate/up + RMSNorm + SwiGLU.
   ProjArgs pg = base_args(c);
   pg.part = part;
-  pg.w[0] = w->w_gate; pg.w[1] = w->w_up;
+  if (w8) {
+    pg.w[0] = w8->w_gate; pg.w[1] = w8->w_up;
+    pg.wscale[0] = w8->s_gate; pg.wscale[1] = w8->s_up;
+  } else {
+    pg.w[0] = w->w_gate; pg.w[1] = w->w_up;
+  }
   pg.N = I; pg.K = H; pg.M = m; pg.y = a;
   if (fuse_norm) {
-    pg.x = h1; pg.gamma = w->ffn_norm;
+    pg.x = h1; pg.gamma = ffn_norm;
   } else {
     timer_before(KID_RMSNORM, s);
-    LL_TRY(launch_rmsnorm(dt, h1, w->ffn_norm, u, m, H, c->eps, s));
+    LL_TRY(launch_rmsnorm(dt, h1, ffn_norm, u, m, H, c->eps, s));
     timer_after(KID_RMSNORM, s);
     pg.x = u;
   }
   timer_before(KID_GEMV_GATEUP, s);
-  LL_TRY(launch_gemv(dt, EPI_SWIGLU, pg, s));
+  LL_TRY(proj(EPI_SWIGLU, pg));
   timer_after(KID_GEMV_GATEUP, s);
 
   // 5. down + residual.
   ProjArgs pd = base_args(c);
   pd.part = part;
-  pd.w[0] = w->w_down; pd.seg1 = pd.seg2 = H;
+  pd.w[0] = w8 ? (const void*)w8->w_down : w->w_down; pd.seg1 = pd.seg2 = H;
+  if (w8) pd.wscale[0] = w8->s_down;
   pd.N = H; pd.K = I; pd.M = m; pd.x = a; pd.resid = h1; pd.y = ym;
   timer_before(KID_GEMV_DOWN, s);
-  LL_TRY(launch_gemv(dt, EPI_RESID, pd, s));
+  LL_TRY(proj(EPI_RESID, pd));
   timer_after(KID_GEMV_DOWN, s);
   return LL_OK;
 }
@@ -411,7 +432,7 @@ int llama_layer_prefill(const ll_config* cfg, const ll_weights* w, const void* x
   for (int b = 0; b < batch; ++b) {
     for (int t0 = 0; t0 < tokens; t0 += 32) {
       const int m = std::min(32, tokens - t0);
-      rc = run_skinny(cfg, w, x, y, k_cache, v_cache, nullptr, start_pos, tokens, 0, s_max,
+      rc = run_skinny(cfg, w, nullptr, x, y, k_cache, v_cache, nullptr, start_pos, tokens, 0, s_max,
                       (int64_t)b * tokens + t0, m, (uint8_t*)ws, L, s);
       if (rc) return rc;
     }
@@ -440,7 +461,66 @@ int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x,
   (void)hipGetLastError();
   for (int b0 = 0; b0 < batch; b0 += 32) {
     const int m = std::min(32, batch - b0);
-    rc = run_skinny(cfg, w, x, y, k_cache, v_cache, ctx_len, 0, 1, max_ctx, s_max, b0, m,
+    rc = run_skinny(cfg, w, nullptr, x, y, k_cache, v_cache, ctx_len, 0, 1, max_ctx, s_max, b0,
+                    m, (uint8_t*)ws, L, s);
+    if (rc) return rc;
+  }
+  return LL_OK;
+}
+
+int llama_quantize_w8(const void* w, int8_t* q, float* scale, int32_t rows, int32_t cols,
+                      int32_t dtype, void* stream) {
+  int rc = check_ptrs({w, q});
+  if (rc) return rc;
+  if ((rc = check_ptrs4({scale}))) return rc;
+  if (rows <= 0 || cols <= 0 || cols % 16 || dtype < LL_F32 || dtype > LL_F16) return LL_EINVAL;
+  (void)hipGetLastError();
+  if (launch_quantize_w8(dtype, w, q, scale, rows, cols, (hipStream_t)stream) != hipSuccess)
+    return LL_EHIP;
+  return LL_OK;
+}
+
+// Tokens per launch group of the int8 decode: at most 4 (the row kernel),
+// fewer when the activations of the longest K would not fit its LDS stage.
+static int w8_group(const ll_config* c) {
+  const int kmax = std::max(std::max(c->hidden, c->intermediate), c->n_heads * c->head_dim);
+  int g = 4;
+  while (g > 0 && !gemv_w8_fits(c->act_dtype, g, kmax)) --g;
+  return g;
+}
+
+int llama_layer_decode_w8(const ll_config* cfg, const ll_weights_w8* w, const void* x, void* y,
+                          void* k_cache, void* v_cache, const int32_t* ctx_len, int32_t batch,
+                          int32_t max_ctx, int32_t s_max, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w) return LL_ENULL;
+  if ((rc = check_ptrs({w->attn_norm, w->ffn_norm, w->w_q, w->w_k, w->w_v, w->w_o, w->w_gate,
+                        w->w_up, w->w_down, w->rope_cos, w->rope_sin})))
+    return rc;
+  if ((rc = check_ptrs4({w->s_q, w->s_k, w->s_v, w->s_o, w->s_gate, w->s_up, w->s_down})))
+    return rc;
+  if ((rc = check_ptrs({x, y, k_cache, v_cache}))) return rc;
+  if ((rc = check_ptrs4({ctx_len}))) return rc;
+  if (batch <= 0 || max_ctx < 0 || s_max <= 0) return LL_EINVAL;
+  if (cfg->hidden % 16 || cfg->intermediate % 16 || (cfg->n_heads * cfg->head_dim) % 16)
+    return LL_EINVAL;
+  if ((int64_t)max_ctx + 1 > s_max || (int64_t)max_ctx + 1 > cfg->max_pos) return LL_ECACHE_FULL;
+  const int g = w8_group(cfg);
+  if (g < 1) return LL_EUNSUPPORTED;
+  const size_t act = esize(cfg->act_dtype);
+  if (overlap(x, (size_t)batch * cfg->hidden * act, y, (size_t)batch * cfg->hidden * act))
+    return LL_EINVAL;
+  const Layout L = layout(cfg, batch, s_max, false);
+  if (!ws) return LL_EWORKSPACE;
+  if (!aligned16(ws)) return LL_EALIGN;
+  if (ws_bytes < L.total) return LL_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  for (int b0 = 0; b0 < batch; b0 += g) {
+    const int m = std::min(g, batch - b0);
+    rc = run_skinny(cfg, nullptr, w, x, y, k_cache, v_cache, ctx_len, 0, 1, max_ctx, s_max, b0, m,
                     (uint8_t*)ws, L, s);
     if (rc) return rc;
   }

@@ -133,6 +133,11 @@ WORKLOADS = {
     "decode_7b_b1_ctx32768_ntk8": Workload("decode_7b_b1_ctx32768_ntk8", 5, L7B, "bf16", "bf16",
                                            "decode", batch=1, ctx=32768, s_max=32769,
                                            extra={"ntk_scale": 8.0}),
+    # The 7B decode with weight-only INT8 projections (codes and scales made
+    # on the device from the bf16 weights).
+    "decode_7b_b1_ctx4096_w8": Workload("decode_7b_b1_ctx4096_w8", 7, L7B, "bf16", "bf16",
+                                        "decode", batch=1, ctx=4096, s_max=4097,
+                                        extra={"w8": True}),
     # Sampling after the LM head: 32 rows of a 32000-token vocabulary with the
     # pages' dialogue settings and 256 previous ids per row.
     "sample_b32_v32000": Workload("sample_b32_v32000", 6, L70B, "f32", "f32", "sample",

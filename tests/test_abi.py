@@ -187,6 +187,12 @@ def test_glue_validation():
     assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, 0.7, 50, 0.9, 0.0, None) == -1
     assert S(FAKE, None, 0, FAKE, FAKE, -1, 32000, 0.7, 50, 0.9, 1.1, None) == -1
     assert S(FAKE, None, 0, FAKE, FAKE, 0, 32000, 0.7, 50, 0.9, 1.1, None) == 0  # empty: no launch
+    Q = L.llama_quantize_w8
+    assert Q(None, FAKE, FAKE, 4, 32, 1, None) == -2
+    assert Q(FAKE, FAKE + 4, FAKE, 4, 32, 1, None) == -3
+    assert Q(FAKE, FAKE, FAKE, 4, 40, 1, None) == -1      # cols % 16
+    assert Q(FAKE, FAKE, FAKE, 0, 32, 1, None) == -1
+    assert Q(FAKE, FAKE, FAKE, 4, 32, 9, None) == -1      # dtype
     assert L.llama_embed(FAKE, FAKE, FAKE, 0, 256, 512, 1, None) == -1
     assert L.llama_embed(FAKE, FAKE + 2, FAKE, 1, 256, 512, 1, None) == -3
     assert L.llama_embed(FAKE, FAKE, FAKE, 1, 256, 512, 7, None) == -1
