@@ -238,6 +238,24 @@ def bench_stack(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def paged_pools(inp, bs, seed):
+    """The contiguous caches of a decode workload laid out as the blocks of a
+    paged cache, in shuffled pool order: (k_pool, v_pool, block_table)."""
+    batch, nkv, s_max, hd = inp["k_cache"].shape
+    max_blocks = -(-s_max // bs)
+    table = np.random.default_rng(seed).permutation(batch * max_blocks).reshape(batch, max_blocks)
+    pools = []
+    for name in ("k_cache", "v_cache"):
+        c = inp[name]
+        pool = np.zeros((batch * max_blocks, nkv, bs, hd), dtype=c.dtype)
+        for b in range(batch):
+            for i in range(max_blocks):
+                lo, hi = i * bs, min((i + 1) * bs, s_max)
+                pool[table[b, i], :, :hi - lo] = c[b, :, lo:hi]
+        pools.append(pool)
+    return pools[0], pools[1], table.astype(np.int32)
+
+
 def bench_sample(args, wl):
     """Sampling after the LM head: one step = one llama_sample call over the
     batch.  The logits come straight from the LM head in a real step, so one
@@ -317,7 +335,8 @@ def main():
     ap.add_argument("--workload", default="decode_7b_b1_ctx4096",
                     choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
                              "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8",
-                             "sample_b32_v32000", "decode_7b_b1_ctx4096_w8"])
+                             "sample_b32_v32000", "decode_7b_b1_ctx4096_w8",
+                             "decode_70b_b32_ragged_paged"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -369,7 +388,7 @@ def main():
     else:
         B.llama_rope_table_ntk(rc, rs, max_pos, s.head_dim, s.rope_theta, ntk)
     w8 = bool(wl.extra.get("w8"))
-    sets = []
+    sets, tables = [], []
     for c in range(copies):
         w = {k: dev(v, act) for k, v in stored.items()}
         w["rope_cos"], w["rope_sin"] = rc, rs
@@ -384,21 +403,33 @@ def main():
             lw = B.LayerWeightsW8(w)
         else:
             lw = B.LayerWeights(w)
-        sets.append((lw, dev(inp["k_cache"], kvd), dev(inp["v_cache"], kvd)))
+        if wl.extra.get("block_size"):
+            kp, vp, table = paged_pools(inp, wl.extra["block_size"], 1000 + c)
+            sets.append((lw, dev(kp, kvd), dev(vp, kvd)))
+            tables.append(torch.from_numpy(table).cuda())
+        else:
+            sets.append((lw, dev(inp["k_cache"], kvd), dev(inp["v_cache"], kvd)))
     decode = wl.phase == "decode"
     if decode:
         x = dev(inp["x"], act)
         y = torch.empty_like(x)
         ctx = torch.from_numpy(inp["ctx_len"]).cuda()
         max_ctx = int(inp["ctx_len"].max())
-        ws = torch.empty(B.llama_layer_workspace_size(cfg, wl.batch, 1, wl.s_max), dtype=torch.uint8,
+        bsz = wl.extra.get("block_size")
+        s_ws = -(-wl.s_max // bsz) * bsz if bsz else wl.s_max  # positions a block table spans
+        ws = torch.empty(B.llama_layer_workspace_size(cfg, wl.batch, 1, s_ws), dtype=torch.uint8,
                          device="cuda")
 
         run = B.llama_layer_decode_w8 if w8 else B.llama_layer_decode
+        bs = wl.extra.get("block_size")
 
         def step(i):
             lw, kc, vc = sets[i % copies]
-            run(cfg, lw, x, y, kc, vc, ctx, wl.batch, max_ctx, wl.s_max, ws)
+            if bs:
+                B.llama_layer_decode_paged(cfg, lw, x, y, kc, vc, bs, tables[i % copies], ctx,
+                                           wl.batch, max_ctx, ws)
+            else:
+                run(cfg, lw, x, y, kc, vc, ctx, wl.batch, max_ctx, wl.s_max, ws)
         # the kernel moving the most bytes: gate/up, or attention at long contexts
         by0 = decode_bytes(s, inp["ctx_len"], act_b, kv_b, w8)
         dom = "attn_decode" if by0["attn_decode"] > by0["gemv_gate_up"] else "gemv_gate_up"
@@ -479,6 +510,8 @@ def main():
         out["config"]["rope_ntk_scale"] = wl.extra["ntk_scale"]
     if wl.extra.get("w8"):
         out["config"]["weights"] = "int8 codes, float32 scale per row"
+    if wl.extra.get("block_size"):
+        out["config"]["kv_cache"] = f"paged, {wl.extra['block_size']}-position blocks, shuffled pool"
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:

@@ -138,6 +138,47 @@ int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x,
                        int32_t max_ctx, int32_t s_max, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Paged KV cache ("Llama2架构全景解析" §2.3 and §3.1: paging the KV cache ends
+ * fragmentation and lets batch 32 fit where batch 4 ran out of memory;
+ * "LLM架构全景解析" §2.2: a memory pool instead of per-request allocation).
+ * The cache of every sequence lives in fixed-size blocks of a shared pool:
+ *   k_pool, v_pool  DEVICE [n_blocks, n_kv_heads, block_size, head_dim] in
+ *                   kv_dtype (one block holds block_size positions of every
+ *                   KV head), 16-byte aligned
+ *   block_table     DEVICE int32 [batch, max_blocks]: block_table[b][i] is the
+ *                   pool block holding positions [i*block_size,
+ *                   (i+1)*block_size) of sequence b; entries outside
+ *                   [0, n_blocks) are clamped into it (the caller owns the
+ *                   table and keeps it valid; the library never reads past
+ *                   the pool)
+ *   block_size      a power of two in [16, 1024]
+ * llama_layer_decode_paged is llama_layer_decode over such a cache: the same
+ * arithmetic in the same order, so its results equal the contiguous cache's
+ * bit for bit.  A sequence can address max_blocks * block_size positions
+ * (max_ctx + 1 must fit; else LL_ECACHE_FULL); the workspace is
+ * llama_layer_workspace_size(cfg, batch, 1, max_blocks * block_size).
+ */
+int llama_layer_decode_paged(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                             void* k_pool, void* v_pool, int32_t n_blocks, int32_t block_size,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* ctx_len, int32_t batch, int32_t max_ctx, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Copies positions [start, start + count) of every sequence and KV head of
+ * contiguous caches k_src, v_src [batch, n_kv_heads, s_max, head_dim] into a
+ * paged cache (arguments as above), e.g. after llama_layer_prefill on a
+ * contiguous scratch cache.  head_dim * element size must be a multiple of
+ * 16 bytes.  Errors: LL_ENULL, LL_EALIGN, LL_EINVAL, LL_ECACHE_FULL
+ * (start + count beyond s_max or max_blocks * block_size), LL_EHIP.
+ */
+int llama_kv_pages_write(const void* k_src, const void* v_src, int32_t s_max, int32_t start,
+                         int32_t count, void* k_pool, void* v_pool, int32_t n_blocks,
+                         int32_t block_size, const int32_t* block_table, int32_t max_blocks,
+                         int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t kv_dtype,
+                         void* stream);
+
+/*
  * Weight-only INT8 ("Llama2架构与推理全解析" §3.2: one byte per weight instead
  * of two halves the weight memory at a small loss of precision).  Symmetric
  * round-to-nearest per output row:

@@ -78,6 +78,12 @@ def lib() -> ctypes.CDLL:
         L.llama_rope_table_ntk.restype = ctypes.c_int
         L.llama_sample.argtypes = [P, P, I32, P, P, I32, I32, F, I32, F, F, P]
         L.llama_sample.restype = ctypes.c_int
+        L.llama_layer_decode_paged.argtypes = [CP, WP, P, P, P, P, I32, I32, P, I32, P, I32, I32,
+                                               P, SZ, P]
+        L.llama_layer_decode_paged.restype = ctypes.c_int
+        L.llama_kv_pages_write.argtypes = [P, P, I32, I32, I32, P, P, I32, I32, P, I32, I32, I32,
+                                           I32, I32, P]
+        L.llama_kv_pages_write.restype = ctypes.c_int
         L.llama_quantize_w8.argtypes = [P, P, P, I32, I32, I32, P]
         L.llama_quantize_w8.restype = ctypes.c_int
         L.llama_layer_decode_w8.argtypes = [CP, ctypes.POINTER(ll_weights_w8), P, P, P, P, P,
@@ -176,6 +182,31 @@ class LayerWeightsW8:
     def __init__(self, tensors: dict):
         self.tensors = dict(tensors)
         self.struct = ll_weights_w8(*[_ptr(self.tensors[n]) for n in self.NAMES])
+
+
+def llama_layer_decode_paged(cfg, weights: LayerWeights, x, y, k_pool, v_pool, block_size,
+                             block_table, ctx_len, batch, max_ctx, ws, ws_bytes=None,
+                             stream=None) -> None:
+    """k_pool, v_pool [n_blocks, n_kv_heads, block_size, head_dim]; block_table
+    [batch, max_blocks] int32; all device tensors."""
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    rc = lib().llama_layer_decode_paged(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x),
+                                        _ptr(y), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                        block_size, _ptr(block_table), block_table.shape[1],
+                                        _ptr(ctx_len), batch, max_ctx, _ptr(ws), nbytes,
+                                        _stream(stream))
+    _check(rc, "llama_layer_decode_paged")
+
+
+def llama_kv_pages_write(k_src, v_src, start, count, k_pool, v_pool, block_size, block_table,
+                         kv_dtype, stream=None) -> None:
+    """k_src, v_src [batch, n_kv_heads, s_max, head_dim] into the pools."""
+    batch, nkv, s_max, hd = k_src.shape
+    _check(lib().llama_kv_pages_write(_ptr(k_src), _ptr(v_src), s_max, start, count, _ptr(k_pool),
+                                      _ptr(v_pool), k_pool.shape[0], block_size,
+                                      _ptr(block_table), block_table.shape[1], batch, nkv, hd,
+                                      DTYPE_CODE[kv_dtype], _stream(stream)),
+           "llama_kv_pages_write")
 
 
 def llama_quantize_w8(w, q, scale, dtype, stream=None) -> None:

@@ -56,24 +56,39 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnDecodeArgs a) {
   const int sub = tid % LPK, slot = tid / LPK;
 
   // Issue every K and V load of this thread first.
-  const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD + sub * 8;
-  const T* kp = reinterpret_cast<const T*>(a.kc) + head_off;
-  const T* vp = reinterpret_cast<const T*>(a.vc) + head_off;
+  const T* kp = reinterpret_cast<const T*>(a.kc) + sub * 8;
+  const T* vp = reinterpret_cast<const T*>(a.vc) + sub * 8;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  // Row of each key; keys past the chunk are not loaded.  Paged caches: when
+  // a pass of KPI keys sits in one block, its block index is wave-uniform.
+  size_t rows[KPT];
+  const bool uniform_pass = a.pages.table && KPI <= (1 << a.pages.log2_bs);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int key = k_lo + slot + i * KPI;
+    const int kk = key < k_hi ? key : k_lo;
+    if (uniform_pass) {
+      const int blk = kv_block_uniform(a.pages, b, min(k_lo + i * KPI, k_hi - 1));
+      rows[i] = ((((size_t)blk * a.nkv + j) << a.pages.log2_bs) +
+                 (kk & ((1 << a.pages.log2_bs) - 1))) * HD;
+    } else {
+      rows[i] = kv_row(a.pages, b, j, kk, a.nkv, a.s_max, HD);
+    }
+  }
   u32x4 kr[KPT][NC], vr[KPT][NC];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int key = k_lo + slot + i * KPI;
     const bool ok = key < k_hi;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[i][c] = ok ? ld16_stream(kp + (size_t)key * HD + c * (8 / NC)) : zero;
+    for (int c = 0; c < NC; ++c) kr[i][c] = ok ? ld16_stream(kp + rows[i] + c * (8 / NC)) : zero;
   }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int key = k_lo + slot + i * KPI;
     const bool ok = key < k_hi;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[i][c] = ok ? ld16_stream(vp + (size_t)key * HD + c * (8 / NC)) : zero;
+    for (int c = 0; c < NC; ++c) vr[i][c] = ok ? ld16_stream(vp + rows[i] + c * (8 / NC)) : zero;
   }
 
   float qf[GC][8];
@@ -249,9 +264,8 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
   const int r16 = lane & 15, g4 = lane >> 4;
   uint8_t* kring = lds + wave * WAVE_LDS;  // [2][TILE]
   uint8_t* vring = kring + 2 * TILE;       // [2][TILE]
-  const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD;
-  const T* kp = reinterpret_cast<const T*>(a.kc) + head_off;
-  const T* vp = reinterpret_cast<const T*>(a.vc) + head_off;
+  const T* kp = reinterpret_cast<const T*>(a.kc);
+  const T* vp = reinterpret_cast<const T*>(a.vc);
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
   // The queries, before any DMA is in flight.  Lanes past GC read head h0 and
@@ -278,14 +292,27 @@ void attn_gqa_kernel(AttnDecodeArgs a) {
   // issues the same 2 TI loads (past the end they repeat the last row), so
   // the wait counts below are exact.  DMA instruction i fills rows
   // RPI i + l / CPR; lane l fetches the row's logical chunk (l % CPR) ^ swz.
+  // Paged caches: a wave's 16 keys (16-aligned) sit in one block of at least
+  // 16 positions, and rows clamped to the last key stay in it, so the block
+  // index is wave-uniform and comes from a scalar load.
   auto load_tile = [&](const T* src, uint8_t* dst, int it, bool is_k) {
     const int kb = k_lo + WI * it + KW * wave;
+    size_t base;  // element offset of row 0 of the key's block, or of the head
+    int kmask;
+    if (a.pages.table) {
+      const int blk = kv_block_uniform(a.pages, b, min(kb, k_hi - 1));
+      base = (((size_t)blk * a.nkv + j) << a.pages.log2_bs) * HD;
+      kmask = (1 << a.pages.log2_bs) - 1;
+    } else {
+      base = ((size_t)b * a.nkv + j) * a.s_max * HD;
+      kmask = -1;
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int r = i * RPI + lane / CPR;
-      const uint32_t key = (uint32_t)min(kb + r, k_hi - 1);
+      const int key = min(kb + r, k_hi - 1);
       const int c = (lane % CPR) ^ (is_k ? (r & (CPR - 1)) : 2 * (r & 3));
-      dma16_stream(src + (key * HD + c * 8), dst + i * 1024);
+      dma16_stream(src + (base + (size_t)(key & kmask) * HD + c * 8), dst + i * 1024);
     }
   };
   // K fragment of slice s: row r16, logical chunk 4s + g4.

@@ -31,7 +31,8 @@ __device__ __forceinline__ int token_position(const ProjArgs& a, int b, int t) {
 // QKV epilogue for four consecutive output features f..f+3 (f % 4 == 0) of
 // global token n (row nl of this launch).  Features [0, nh*hd) are q, then nkv*hd of k, then v.
 // q and k pairs (2i, 2i+1) are turned by pos * theta_i using the float32
-// cos/sin tables; k and v are written into the caches at `pos`.
+// cos/sin tables; k and v are written into the caches at `pos` (contiguous,
+// or through the block table of a paged cache).
 template <int DT>
 __device__ __forceinline__ void qkv_epilogue4(const ProjArgs& a, int n, int nl, int f, float* v) {
   const int b = n / a.T;
@@ -61,11 +62,11 @@ __device__ __forceinline__ void qkv_epilogue4(const ProjArgs& a, int n, int nl, 
     }
   } else if (f < qdim + kdim) {
     const int j = (f - qdim) / hd, d = (f - qdim) - j * hd;
-    const size_t idx = (((size_t)b * a.nkv + j) * a.s_max + pos) * hd + d;
+    const size_t idx = kv_row(a.pages, b, j, pos, a.nkv, a.s_max, hd) + d;
     store4_rt(a.kc, idx, a.kv_dt, v[0], v[1], v[2], v[3]);
   } else {
     const int j = (f - qdim - kdim) / hd, d = (f - qdim - kdim) - j * hd;
-    const size_t idx = (((size_t)b * a.nkv + j) * a.s_max + pos) * hd + d;
+    const size_t idx = kv_row(a.pages, b, j, pos, a.nkv, a.s_max, hd) + d;
     store4_rt(a.vc, idx, a.kv_dt, v[0], v[1], v[2], v[3]);
   }
 }

@@ -78,6 +78,36 @@ hipError_t launch_argmax(const float* logits, int32_t* ids, int n, int vocab, hi
   return hipGetLastError();
 }
 
+// Copy of positions [start, start + count) of contiguous caches into the
+// pools of a paged cache, 16 bytes per thread; grid: (rows of 16-byte chunks,
+// sequence * nkv).
+__global__ __launch_bounds__(256) void kv_pages_write_kernel(const uint8_t* ks, const uint8_t* vs,
+                                                             int s_max, int start, int count,
+                                                             uint8_t* kp, uint8_t* vp, KvPages pg,
+                                                             int nkv, int hd, int esz) {
+  const int bj = blockIdx.y, b = bj / nkv, j = bj - b * nkv;
+  const int cpr = hd * esz / 16;  // 16-byte chunks per row
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= count * cpr) return;
+  const int t = idx / cpr, c = idx - t * cpr;
+  const int pos = start + t;
+  const size_t src = ((((size_t)b * nkv + j) * s_max + pos) * hd) * esz + (size_t)c * 16;
+  const size_t dst = kv_row(pg, b, j, pos, nkv, 0, hd) * esz + (size_t)c * 16;
+  st16(kp + dst, ld16(ks + src));
+  st16(vp + dst, ld16(vs + src));
+}
+
+hipError_t launch_kv_pages_write(const void* k_src, const void* v_src, int s_max, int start,
+                                 int count, void* k_pool, void* v_pool, const KvPages& pg,
+                                 int batch, int nkv, int hd, int kv_dt, hipStream_t s) {
+  const int esz = kv_dt == DT_F32 ? 4 : 2;
+  const int n = count * (hd * esz / 16);
+  LL_LAUNCH(kv_pages_write_kernel, dim3((n + 255) / 256, batch * nkv), dim3(256), 0, s,
+            (const uint8_t*)k_src, (const uint8_t*)v_src, s_max, start, count, (uint8_t*)k_pool,
+            (uint8_t*)v_pool, pg, nkv, hd, esz);
+  return hipGetLastError();
+}
+
 // Weight-only int8 by rows: scale = max|w| / 127, q = rint(w / scale) in
 // [-127, 127] (a zero row: scale 0, codes 0).  One workgroup per row; the
 // division is the correctly rounded float32 one.

@@ -16,6 +16,34 @@ enum Epi {
 };
 
 // Arguments of one projection y[m, n] = sum_k act(x)[m, k] * W[n, k].
+// A paged KV cache: k/v pools [n_blocks, nkv, 1 << log2_bs, hd]; table[b *
+// stride + i] is the pool block holding positions [i << log2_bs, (i+1) <<
+// log2_bs) of sequence b (entries are clamped into [0, n_blocks)).
+struct KvPages {
+  const int32_t* table;
+  int stride, log2_bs, n_blocks;
+};
+
+// Element offset of the row of position `pos` of KV head j of sequence b:
+// contiguous caches [B, nkv, s_max, hd], or through the block table.
+__device__ __forceinline__ size_t kv_row(const KvPages& pg, int b, int j, int pos, int nkv,
+                                         int s_max, int hd) {
+  if (!pg.table) return (((size_t)b * nkv + j) * s_max + pos) * hd;
+  int blk = pg.table[(size_t)b * pg.stride + (pos >> pg.log2_bs)];
+  blk = blk < 0 ? 0 : (blk >= pg.n_blocks ? pg.n_blocks - 1 : blk);
+  return ((((size_t)blk * nkv + j) << pg.log2_bs) + (pos & ((1 << pg.log2_bs) - 1))) * hd;
+}
+
+// Pool block of position `key` of sequence b when both are the same in every
+// lane of the wave: a scalar load (constant address space), which waits on
+// lgkmcnt, so it leaves the vector-memory counts of the DMA pipelines alone.
+__device__ __forceinline__ int kv_block_uniform(const KvPages& pg, int b, int key) {
+  typedef __attribute__((address_space(4))) const int32_t* cptr;
+  const int idx = __builtin_amdgcn_readfirstlane(b * pg.stride + (key >> pg.log2_bs));
+  int blk = ((cptr)pg.table)[idx];
+  return blk < 0 ? 0 : (blk >= pg.n_blocks ? pg.n_blocks - 1 : blk);
+}
+
 struct ProjArgs {
   const void* w[3];   // row segments: [0,seg1) w[0]; [seg1,seg2) w[1]; [seg2,N) w[2]
   int seg1, seg2;     // (EPI_SWIGLU: w[0] = gate, w[1] = up, both N rows)
@@ -38,6 +66,7 @@ struct ProjArgs {
   const float* rsin;
   float* part;        // float32 K-split partials of the streaming projection (workspace)
   const float* wscale[3];  // int8 weights: float32 scale per row of each segment
+  KvPages pages;           // paged caches (pages.table == nullptr: contiguous)
 };
 
 // Decode-sized projection (M <= 32 tokens).  A fused norm (gamma != nullptr)
@@ -50,6 +79,11 @@ bool gemv_fits_lds(int dt, int M, int K);
 constexpr int GEMV_W8_LDS_BYTES = 128 * 1024;
 bool gemv_w8_fits(int dt, int M, int K);
 hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
+// Positions [start, start + count) of every (sequence, KV head) of contiguous
+// caches [B, nkv, s_max, hd] copied into the pools of a paged cache.
+hipError_t launch_kv_pages_write(const void* k_src, const void* v_src, int s_max, int start,
+                                 int count, void* k_pool, void* v_pool, const KvPages& pg,
+                                 int batch, int nkv, int hd, int kv_dt, hipStream_t s);
 // Per-row symmetric int8 codes and float32 scales of a [rows, cols] matrix.
 hipError_t launch_quantize_w8(int dt, const void* w, int8_t* q, float* scale, int rows, int cols,
                               hipStream_t s);
@@ -86,6 +120,7 @@ struct AttnDecodeArgs {
   float* part_l;         // [nq, nh, nsplit]
   float* part_acc;       // [nq, nh, nsplit, hd]
   void* o;               // [nq, nh*hd] act dtype
+  KvPages pages;         // paged caches: kc/vc are the pools, rows of query n's sequence n / T
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
 // Query heads served per workgroup for a GQA group of g heads.

@@ -13,6 +13,7 @@
 //  * "token-wide" (prefill of > 32 tokens in bf16/f16):
 //      RMSNorm, QKV GEMM + RoPE + cache append, causal MFMA attention,
 //      O GEMM + residual, RMSNorm, gate/up GEMM + SwiGLU, down GEMM + residual.
+#include <climits>
 #include <cmath>
 #include <string.h>
 
@@ -194,10 +195,11 @@ static ProjArgs base_args(const ll_config* c) {
 // Token-skinny plan for tokens [tok0, tok0 + m) of B*T.
 // With w8 set (and w unused) the projections take int8 weights and per-row
 // scales through the int8 row kernel; m is then at most 4.
+// With pages.table set, kc and vc are the pools of a paged cache.
 static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_w8* w8,
                       const void* x, void* y, void* kc, void* vc, const int32_t* ctx_len,
                       int start_pos, int T, int max_ctx, int s_max, int64_t tok0, int m,
-                      uint8_t* ws, const Layout& L, hipStream_t s) {
+                      uint8_t* ws, const Layout& L, hipStream_t s, const KvPages& pages = {}) {
   const int dt = c->act_dtype;
   const size_t act = esize(dt);
   const int H = c->hidden, I = c->intermediate;
@@ -241,7 +243,7 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
   }
   p.q32 = (float*)(ws + L.q32);
   p.kc = kc; p.vc = vc; p.ctx_len = ctx_len; p.start_pos = start_pos; p.T = T;
-  p.max_ctx = max_ctx; p.s_max = s_max;
+  p.max_ctx = max_ctx; p.s_max = s_max; p.pages = pages;
   p.rcos = w8 ? w8->rope_cos : w->rope_cos;
   p.rsin = w8 ? w8->rope_sin : w->rope_sin;
   timer_before(KID_GEMV_QKV, s);
@@ -277,8 +279,15 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
     at.start_pos = start_pos + (int)(tok0 % T);
     at.T = m;
   }
-  at.kc = (const uint8_t*)kc + b0 * seq_bytes;
-  at.vc = (const uint8_t*)vc + b0 * seq_bytes;
+  if (pages.table) {
+    at.kc = kc;
+    at.vc = vc;
+    at.pages = pages;
+    at.pages.table = pages.table + b0 * pages.stride;
+  } else {
+    at.kc = (const uint8_t*)kc + b0 * seq_bytes;
+    at.vc = (const uint8_t*)vc + b0 * seq_bytes;
+  }
   timer_before(KID_ATTN_DECODE, s);
   LL_TRY(launch_attn_decode(at, s));
   timer_after(KID_ATTN_DECODE, s);
@@ -465,6 +474,75 @@ int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x,
                     m, (uint8_t*)ws, L, s);
     if (rc) return rc;
   }
+  return LL_OK;
+}
+
+static int check_pages(int32_t n_blocks, int32_t max_blocks, int32_t block_size, int* log2_bs) {
+  if (n_blocks <= 0 || max_blocks <= 0) return LL_EINVAL;
+  int l = 0;
+  while ((1 << l) < block_size && l < 30) ++l;
+  if (block_size < 16 || block_size > 1024 || (1 << l) != block_size) return LL_EINVAL;
+  *log2_bs = l;
+  return LL_OK;
+}
+
+int llama_layer_decode_paged(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                             void* k_pool, void* v_pool, int32_t n_blocks, int32_t block_size,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* ctx_len, int32_t batch, int32_t max_ctx, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if ((rc = check_ptrs({x, y, k_pool, v_pool}))) return rc;
+  if ((rc = check_ptrs4({ctx_len, block_table}))) return rc;
+  int log2_bs = 0;
+  if ((rc = check_pages(n_blocks, max_blocks, block_size, &log2_bs))) return rc;
+  if (batch <= 0 || max_ctx < 0) return LL_EINVAL;
+  const int64_t cap = (int64_t)max_blocks * block_size;
+  if (cap > INT32_MAX) return LL_EINVAL;
+  const int s_max = (int)cap;  // positions a sequence's table can address
+  if ((int64_t)max_ctx + 1 > s_max || (int64_t)max_ctx + 1 > cfg->max_pos) return LL_ECACHE_FULL;
+  const size_t act = esize(cfg->act_dtype);
+  if (overlap(x, (size_t)batch * cfg->hidden * act, y, (size_t)batch * cfg->hidden * act))
+    return LL_EINVAL;
+  const Layout L = layout(cfg, batch, s_max, false);
+  if (!ws) return LL_EWORKSPACE;
+  if (!aligned16(ws)) return LL_EALIGN;
+  if (ws_bytes < L.total) return LL_EWORKSPACE;
+  const KvPages pages{block_table, max_blocks, log2_bs, n_blocks};
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  for (int b0 = 0; b0 < batch; b0 += 32) {
+    const int m = std::min(32, batch - b0);
+    rc = run_skinny(cfg, w, nullptr, x, y, k_pool, v_pool, ctx_len, 0, 1, max_ctx, s_max, b0, m,
+                    (uint8_t*)ws, L, s, pages);
+    if (rc) return rc;
+  }
+  return LL_OK;
+}
+
+int llama_kv_pages_write(const void* k_src, const void* v_src, int32_t s_max, int32_t start,
+                         int32_t count, void* k_pool, void* v_pool, int32_t n_blocks,
+                         int32_t block_size, const int32_t* block_table, int32_t max_blocks,
+                         int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t kv_dtype,
+                         void* stream) {
+  int rc = check_ptrs({k_src, v_src, k_pool, v_pool});
+  if (rc) return rc;
+  if ((rc = check_ptrs4({block_table}))) return rc;
+  int log2_bs = 0;
+  if ((rc = check_pages(n_blocks, max_blocks, block_size, &log2_bs))) return rc;
+  if (batch <= 0 || n_kv_heads <= 0 || head_dim <= 0 || kv_dtype < LL_F32 || kv_dtype > LL_F16 ||
+      (head_dim * (int)esize(kv_dtype)) % 16 || s_max <= 0 || start < 0 || count < 0)
+    return LL_EINVAL;
+  if ((int64_t)start + count > s_max || (int64_t)start + count > (int64_t)max_blocks * block_size)
+    return LL_ECACHE_FULL;
+  if (count == 0) return LL_OK;
+  const KvPages pages{block_table, max_blocks, log2_bs, n_blocks};
+  (void)hipGetLastError();
+  if (launch_kv_pages_write(k_src, v_src, s_max, start, count, k_pool, v_pool, pages, batch,
+                            n_kv_heads, head_dim, kv_dtype, (hipStream_t)stream) != hipSuccess)
+    return LL_EHIP;
   return LL_OK;
 }
 

@@ -133,6 +133,12 @@ WORKLOADS = {
     "decode_7b_b1_ctx32768_ntk8": Workload("decode_7b_b1_ctx32768_ntk8", 5, L7B, "bf16", "bf16",
                                            "decode", batch=1, ctx=32768, s_max=32769,
                                            extra={"ntk_scale": 8.0}),
+    # The 70B batch-32 decode over a paged cache: 64-position blocks of one
+    # pool, in shuffled order (same weights, input and lengths as the
+    # contiguous workload: seed index 3).
+    "decode_70b_b32_ragged_paged": Workload("decode_70b_b32_ragged_paged", 3, L70B, "bf16", "f16",
+                                            "decode", batch=32, ctx_range=(512, 4096), s_max=4097,
+                                            extra={"block_size": 64}),
     # The 7B decode with weight-only INT8 projections (codes and scales made
     # on the device from the bf16 weights).
     "decode_7b_b1_ctx4096_w8": Workload("decode_7b_b1_ctx4096_w8", 7, L7B, "bf16", "bf16",

@@ -187,6 +187,14 @@ def test_glue_validation():
     assert S(FAKE, None, 0, FAKE, FAKE, 4, 32000, 0.7, 50, 0.9, 0.0, None) == -1
     assert S(FAKE, None, 0, FAKE, FAKE, -1, 32000, 0.7, 50, 0.9, 1.1, None) == -1
     assert S(FAKE, None, 0, FAKE, FAKE, 0, 32000, 0.7, 50, 0.9, 1.1, None) == 0  # empty: no launch
+    W = L.llama_kv_pages_write  # k, v, s_max, start, count, kp, vp, n_blocks, bs, table, max_blocks, B, nkv, hd, dt
+    assert W(FAKE, FAKE, 64, 0, 8, FAKE, FAKE, 4, 16, None, 4, 1, 2, 64, 1, None) == -2
+    assert W(FAKE, FAKE, 64, 0, 8, FAKE, FAKE, 4, 24, FAKE, 4, 1, 2, 64, 1, None) == -1  # not 2^k
+    assert W(FAKE, FAKE, 64, 0, 8, FAKE, FAKE, 4, 8, FAKE, 4, 1, 2, 64, 1, None) == -1   # < 16
+    assert W(FAKE, FAKE, 64, 60, 8, FAKE, FAKE, 4, 16, FAKE, 4, 1, 2, 64, 1, None) == -4  # past s_max
+    assert W(FAKE, FAKE, 256, 60, 8, FAKE, FAKE, 4, 16, FAKE, 4, 1, 2, 64, 1, None) == -4  # past pages
+    assert W(FAKE, FAKE, 64, 0, 8, FAKE, FAKE, 0, 16, FAKE, 4, 1, 2, 64, 1, None) == -1   # no blocks
+    assert W(FAKE, FAKE, 64, 0, 0, FAKE, FAKE, 4, 16, FAKE, 4, 1, 2, 64, 1, None) == 0    # nothing
     Q = L.llama_quantize_w8
     assert Q(None, FAKE, FAKE, 4, 32, 1, None) == -2
     assert Q(FAKE, FAKE + 4, FAKE, 4, 32, 1, None) == -3
