@@ -131,6 +131,19 @@ def test_paged_f32_cache_single_block():
     run_paged_case("paged-f32", S.TINY, "f32", "f32", [3, 20, 23], 24, 256, 153, oracle=True)
 
 
+def test_paged_batch_over_32_and_full_table():
+    # 40 sequences: two launch groups (32 + 8), the second reading its block
+    # table rows from an offset; one context on the table's last position
+    ctx = list(np.random.default_rng(4).integers(0, 255, 40))
+    ctx[37] = 255
+    run_paged_case("paged-b40", S.Shape(256, 4, 1, 64, 688), "bf16", "bf16", ctx, 256, 16, 155)
+
+
+def test_paged_largest_block():
+    run_paged_case("paged-bs1024", S.Shape(512, 8, 2, 128, 1376), "bf16", "f16", [100, 1500, 2047],
+                   2048, 1024, 156)
+
+
 def test_paged_70b_b32_full():
     """The benchmark's batched decode, 64-position blocks in a shuffled pool."""
     name = "decode_70b_b32_ragged"
