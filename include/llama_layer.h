@@ -165,6 +165,21 @@ int llama_layer_decode_paged(const ll_config* cfg, const ll_weights* w, const vo
                              size_t ws_bytes, void* stream);
 
 /*
+ * llama_layer_prefill over a paged cache (arguments as llama_layer_decode_paged
+ * and llama_layer_prefill): positions start_pos .. start_pos + tokens - 1 of
+ * every sequence are appended through its block table, and attention reads
+ * the earlier positions from the pages, so a prompt can be prefilled in
+ * chunks.  Results equal llama_layer_prefill's on a contiguous cache bit for
+ * bit; the workspace is llama_layer_workspace_size(cfg, batch, tokens,
+ * max_blocks * block_size).
+ */
+int llama_layer_prefill_paged(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                              void* k_pool, void* v_pool, int32_t n_blocks, int32_t block_size,
+                              const int32_t* block_table, int32_t max_blocks, int32_t batch,
+                              int32_t tokens, int32_t start_pos, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
  * Copies positions [start, start + count) of every sequence and KV head of
  * contiguous caches k_src, v_src [batch, n_kv_heads, s_max, head_dim] into a
  * paged cache (arguments as above), e.g. after llama_layer_prefill on a

@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.llama_layer_decode_paged.argtypes = [CP, WP, P, P, P, P, I32, I32, P, I32, P, I32, I32,
                                                P, SZ, P]
         L.llama_layer_decode_paged.restype = ctypes.c_int
+        L.llama_layer_prefill_paged.argtypes = [CP, WP, P, P, P, P, I32, I32, P, I32, I32, I32,
+                                                I32, P, SZ, P]
+        L.llama_layer_prefill_paged.restype = ctypes.c_int
         L.llama_kv_pages_write.argtypes = [P, P, I32, I32, I32, P, P, I32, I32, P, I32, I32, I32,
                                            I32, I32, P]
         L.llama_kv_pages_write.restype = ctypes.c_int
@@ -196,6 +199,18 @@ def llama_layer_decode_paged(cfg, weights: LayerWeights, x, y, k_pool, v_pool, b
                                         _ptr(ctx_len), batch, max_ctx, _ptr(ws), nbytes,
                                         _stream(stream))
     _check(rc, "llama_layer_decode_paged")
+
+
+def llama_layer_prefill_paged(cfg, weights: LayerWeights, x, y, k_pool, v_pool, block_size,
+                              block_table, batch, tokens, start_pos, ws, ws_bytes=None,
+                              stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    rc = lib().llama_layer_prefill_paged(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x),
+                                         _ptr(y), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                         block_size, _ptr(block_table), block_table.shape[1],
+                                         batch, tokens, start_pos, _ptr(ws), nbytes,
+                                         _stream(stream))
+    _check(rc, "llama_layer_prefill_paged")
 
 
 def llama_kv_pages_write(k_src, v_src, start, count, k_pool, v_pool, block_size, block_table,

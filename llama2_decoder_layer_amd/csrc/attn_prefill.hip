@@ -63,9 +63,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
   for (int s = 0; s < HD / 16; ++s) qf[s] = (my_t < T) ? ld16(qp + s * 16 + h2 * 8) : zero;
 
-  const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD;
-  const ET* kbase = reinterpret_cast<const ET*>(a.kc) + head_off;
-  const ET* vbase = reinterpret_cast<const ET*>(a.vc) + head_off;
+  const ET* kbase = reinterpret_cast<const ET*>(a.kc);
+  const ET* vbase = reinterpret_cast<const ET*>(a.vc);
 
   f32x16 oacc[HD / 32];
 #pragma unroll
@@ -84,7 +83,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
       const int idx = tid + i * 256;
       const int kr = idx / CPR, c = idx - kr * CPR;
       const int key = key0 + kr;
-      const u32x4 v = (key < kv_end) ? ld16(kbase + (size_t)key * HD + c * 8) : zero;
+      const u32x4 v = (key < kv_end)
+          ? ld16(kbase + kv_row(a.pages, b, j, key, a.nkv, a.s_max, HD) + c * 8) : zero;
       st16(&lds_k[kr * HD + ((c ^ ksw(kr)) << 3)], v);
     }
     // V tile -> LDS transposed: thread takes KPT keys x 8 dims.
@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KPT; ++kk) {
         const int key = key0 + kg * KPT + kk;
-        const u32x4 v = (key < kv_end) ? ld16(vbase + (size_t)key * HD + dc * 8) : zero;
+        const u32x4 v = (key < kv_end)
+            ? ld16(vbase + kv_row(a.pages, b, j, key, a.nkv, a.s_max, HD) + dc * 8) : zero;
 #pragma unroll
         for (int w = 0; w < 4; ++w) e16[kk][w] = v[w];
       }
@@ -259,25 +260,38 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
 #pragma unroll
   for (int s = 0; s < HD / 16; ++s) qf[s] = (my_t < T) ? ld16(qp + s * 16 + h2 * 8) : zero;
 
-  const size_t head_off = ((size_t)b * a.nkv + j) * a.s_max * HD;
-  const ET* kbase = reinterpret_cast<const ET*>(a.kc) + head_off;
-  const ET* vbase = reinterpret_cast<const ET*>(a.vc) + head_off;
+  const ET* kbase = reinterpret_cast<const ET*>(a.kc);
+  const ET* vbase = reinterpret_cast<const ET*>(a.vc);
 
   // DMA: instruction i of wave w fills rows 16w + 4i + (lane >> 4), physical
   // chunk lane & 15.  Rows past kv_end read the last needed row (finite; those
-  // keys are masked).
+  // keys are masked).  A paged cache: the wave's 16 rows are 16-aligned keys
+  // (or all the clamped last key) inside one block of at least 16 positions,
+  // so the block index is wave-uniform and comes from a scalar load, which
+  // leaves the DMA wait counts alone.
   const int rsub = lane >> 4, pch = lane & 15;
   const int vcol = (pch ^ (4 * rsub)) * 8;  // (16w + 4i + rsub) & 3 == rsub
   auto issue = [&](int buf, int key0) {
     uint8_t* kb = lds + buf * STAGE_B;
     uint8_t* vb = kb + TILE_B;
+    size_t base;
+    int kmask;
+    if (a.pages.table) {
+      const int blk = kv_block_uniform(a.pages, b, min(key0 + 16 * wave, kv_end - 1));
+      base = (((size_t)blk * a.nkv + j) << a.pages.log2_bs) * HD;
+      kmask = (1 << a.pages.log2_bs) - 1;
+    } else {
+      base = ((size_t)b * a.nkv + j) * a.s_max * HD;
+      kmask = -1;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wave + 4 * i + rsub;
       const int key = min(key0 + r, kv_end - 1);
       const int kcol = (pch ^ (r & 15)) * 8;
-      dma16(kbase + (size_t)key * HD + kcol, kb + (16 * wave + 4 * i) * ROWB);
-      dma16(vbase + (size_t)key * HD + vcol, vb + (16 * wave + 4 * i) * ROWB);
+      const size_t row = base + (size_t)(key & kmask) * HD;
+      dma16(kbase + row + kcol, kb + (16 * wave + 4 * i) * ROWB);
+      dma16(vbase + row + vcol, vb + (16 * wave + 4 * i) * ROWB);
     }
   };
 

@@ -55,7 +55,7 @@ __device__ __forceinline__ void gemm_qkv_store(const ProjArgs& a, int b, int t, 
     const int g = f < qd + kd ? f - qd : f - qd - kd;
     const int j = g / hd;
     KT* cache = reinterpret_cast<KT*>(f < qd + kd ? a.kc : a.vc);
-    dst = cache + (((size_t)b * a.nkv + j) * a.s_max + pos) * hd + (g - j * hd);
+    dst = cache + kv_row(a.pages, b, j, pos, a.nkv, a.s_max, hd) + (g - j * hd);
   }
   store4<KVDT>(dst, v[0], v[1], v[2], v[3]);
 }

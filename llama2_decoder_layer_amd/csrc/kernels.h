@@ -143,6 +143,7 @@ struct AttnPrefillArgs {
   const void* vc;
   void* o;         // [B, T, nh*hd] in format out_dt
   int B, T, start_pos, nh, nkv, hd, s_max, dt, out_dt;
+  KvPages pages;   // paged caches: kc/vc are the pools (block_size >= 16)
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 

@@ -338,7 +338,8 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
 
 static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void* y, void* kc,
                     void* vc, int B, int T, int start_pos, int s_max, uint8_t* ws,
-                    const Layout& L, hipStream_t s) {
+                    const Layout& L, hipStream_t s,
+                    const KvPages& pages = {}) {
   const int dt = c->act_dtype;
   const int H = c->hidden, I = c->intermediate;
   const int qd = c->n_heads * c->head_dim, kd = c->n_kv_heads * c->head_dim;
@@ -356,6 +357,7 @@ static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void
   p.seg1 = qd; p.seg2 = qd + kd;
   p.N = qd + 2 * kd; p.K = H; p.M = M; p.x = u;
   p.q16 = ws + L.q16; p.kc = kc; p.vc = vc; p.start_pos = start_pos; p.T = T;
+  p.pages = pages;
   p.s_max = s_max; p.rcos = w->rope_cos; p.rsin = w->rope_sin;
   timer_before(KID_GEMM_QKV, s);
   LL_TRY(launch_gemm(dt, EPI_QKV, p, s));
@@ -365,6 +367,7 @@ static int run_wide(const ll_config* c, const ll_weights* w, const void* x, void
   ap.q = ws + L.q16; ap.kc = kc; ap.vc = vc; ap.o = ws + L.o;
   ap.B = B; ap.T = T; ap.start_pos = start_pos; ap.nh = c->n_heads; ap.nkv = c->n_kv_heads;
   ap.hd = c->head_dim; ap.s_max = s_max; ap.dt = c->kv_dtype; ap.out_dt = dt;
+  ap.pages = pages;
   timer_before(KID_ATTN_PREFILL, s);
   LL_TRY(launch_attn_prefill(ap, s));
   timer_after(KID_ATTN_PREFILL, s);
@@ -414,13 +417,12 @@ size_t llama_layer_workspace_size(const ll_config* cfg, int32_t batch, int32_t t
   return need;
 }
 
-int llama_layer_prefill(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+// Prefill over contiguous caches, or (pages.table set) the pools of a paged
+// cache whose tables address s_max positions per sequence.
+static int prefill_impl(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
                         void* k_cache, void* v_cache, int32_t batch, int32_t tokens,
-                        int32_t start_pos, int32_t s_max, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_config(cfg);
-  if (rc) return rc;
-  if ((rc = check_weights(w))) return rc;
-  if ((rc = check_ptrs({x, y, k_cache, v_cache}))) return rc;
+                        int32_t start_pos, int32_t s_max, void* ws, size_t ws_bytes, void* stream,
+                        const KvPages& pages) {
   if (batch <= 0 || tokens <= 0 || start_pos < 0 || s_max <= 0) return LL_EINVAL;
   if ((int64_t)start_pos + tokens > s_max || (int64_t)start_pos + tokens > cfg->max_pos)
     return LL_ECACHE_FULL;
@@ -436,17 +438,29 @@ int llama_layer_prefill(const ll_config* cfg, const ll_weights* w, const void* x
   (void)hipGetLastError();
   if (wide)
     return run_wide(cfg, w, x, y, k_cache, v_cache, batch, tokens, start_pos, s_max,
-                    (uint8_t*)ws, L, s);
+                    (uint8_t*)ws, L, s, pages);
   // Token-skinny prefill: groups of <= 32 tokens that never straddle sequences.
   for (int b = 0; b < batch; ++b) {
     for (int t0 = 0; t0 < tokens; t0 += 32) {
       const int m = std::min(32, tokens - t0);
-      rc = run_skinny(cfg, w, nullptr, x, y, k_cache, v_cache, nullptr, start_pos, tokens, 0, s_max,
-                      (int64_t)b * tokens + t0, m, (uint8_t*)ws, L, s);
+      const int rc = run_skinny(cfg, w, nullptr, x, y, k_cache, v_cache, nullptr, start_pos,
+                                tokens, 0, s_max, (int64_t)b * tokens + t0, m, (uint8_t*)ws, L, s,
+                                pages);
       if (rc) return rc;
     }
   }
   return LL_OK;
+}
+
+int llama_layer_prefill(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                        void* k_cache, void* v_cache, int32_t batch, int32_t tokens,
+                        int32_t start_pos, int32_t s_max, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if ((rc = check_ptrs({x, y, k_cache, v_cache}))) return rc;
+  return prefill_impl(cfg, w, x, y, k_cache, v_cache, batch, tokens, start_pos, s_max, ws,
+                      ws_bytes, stream, KvPages{});
 }
 
 int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
@@ -520,6 +534,24 @@ int llama_layer_decode_paged(const ll_config* cfg, const ll_weights* w, const vo
     if (rc) return rc;
   }
   return LL_OK;
+}
+
+int llama_layer_prefill_paged(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                              void* k_pool, void* v_pool, int32_t n_blocks, int32_t block_size,
+                              const int32_t* block_table, int32_t max_blocks, int32_t batch,
+                              int32_t tokens, int32_t start_pos, void* ws, size_t ws_bytes,
+                              void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if ((rc = check_ptrs({x, y, k_pool, v_pool}))) return rc;
+  if ((rc = check_ptrs4({block_table}))) return rc;
+  int log2_bs = 0;
+  if ((rc = check_pages(n_blocks, max_blocks, block_size, &log2_bs))) return rc;
+  const int64_t cap = (int64_t)max_blocks * block_size;
+  if (cap > INT32_MAX) return LL_EINVAL;
+  return prefill_impl(cfg, w, x, y, k_pool, v_pool, batch, tokens, start_pos, (int32_t)cap, ws,
+                      ws_bytes, stream, KvPages{block_table, max_blocks, log2_bs, n_blocks});
 }
 
 int llama_kv_pages_write(const void* k_src, const void* v_src, int32_t s_max, int32_t start,

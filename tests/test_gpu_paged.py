@@ -154,6 +154,58 @@ def test_paged_70b_b32_full():
                    wl.s_max, 64, 154, stored=stored, inp=inp)
 
 
+def run_paged_prefill_case(label, shape, act, kv, batch, tokens, start_pos, s_max, bs, seed):
+    """Prefill over a paged cache whose first start_pos positions hold earlier
+    tokens, against the same prefill on the contiguous cache: bit for bit."""
+    say(f"[{label}] paged prefill B={batch} T={tokens} start={start_pos} s_max={s_max} block={bs} "
+        f"{act}/{kv} {shape}")
+    stored = random_layer(shape, act, seed)
+    inp = S.draw_prefill_inputs(np.random.SeedSequence(seed + 1), shape, batch, tokens, s_max,
+                                act, kv, start_pos)
+    dl = DeviceLayer(shape, stored, act, kv, max_pos=s_max)
+    x = to_dev(inp["x"], act)
+    kc, vc = to_dev(inp["k_cache"], kv), to_dev(inp["v_cache"], kv)
+    y_ref = dl.prefill(x, kc, vc, batch, tokens, start_pos, s_max)
+    table, n_blocks, max_blocks = make_pages(batch, shape.n_kv_heads, s_max, shape.head_dim, bs,
+                                             kv, seed + 7)
+    fill = np.array(0x7FC0 if kv != "f32" else np.nan, dtype=STORAGE[kv])
+    kp = to_dev(scatter(inp["k_cache"], table, n_blocks, bs, fill), kv)
+    vp = to_dev(scatter(inp["v_cache"], table, n_blocks, bs, fill), kv)
+    y = torch.full_like(x, float("nan"))
+    ws = dl.workspace(batch, tokens, max_blocks * bs)
+    B.llama_layer_prefill_paged(dl.cfg, dl.weights, x, y, kp, vp, bs,
+                                torch.from_numpy(table).cuda(), batch, tokens, start_pos, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(y), from_dev(y_ref)), f"{label}: paged prefill differs"
+    view = torch.int16 if kv != "f32" else torch.float32
+    gk = gather(kp.view(view).cpu().numpy().view(STORAGE[kv]), table, s_max)
+    gv = gather(vp.view(view).cpu().numpy().view(STORAGE[kv]), table, s_max)
+    rk = kc.view(view).cpu().numpy().view(STORAGE[kv])
+    rv = vc.view(view).cpu().numpy().view(STORAGE[kv])
+    new = slice(start_pos, start_pos + tokens)
+    assert np.array_equal(gk[:, :, new], rk[:, :, new]) and np.array_equal(gv[:, :, new],
+                                                                            rv[:, :, new])
+    assert np.array_equal(gk[:, :, :start_pos], rk[:, :, :start_pos])
+    say(f"[{label}] paged prefill == contiguous, bit for bit (output and appended entries)")
+
+
+def test_paged_prefill_wide_hd128_chunked():
+    # MFMA prefill (head_dim 128, DMA key tiles) after 200 cached positions, 2 sequences
+    run_paged_prefill_case("paged-prefill-hd128", S.Shape(512, 8, 2, 128, 1032), "bf16", "bf16",
+                           2, 300, 200, 512, 32, 170)
+
+
+def test_paged_prefill_wide_hd64_f16():
+    run_paged_prefill_case("paged-prefill-hd64", S.Shape(256, 4, 1, 64, 512), "bf16", "f16", 1,
+                           150, 70, 256, 16, 171)
+
+
+def test_paged_prefill_skinny():
+    # 2 x 16 tokens: the token-skinny plan (decode attention kernels in prefill mode)
+    run_paged_prefill_case("paged-prefill-16", S.Shape(256, 4, 2, 64, 688), "bf16", "bf16", 2, 16,
+                           45, 96, 16, 172)
+
+
 def test_kv_pages_write():
     r = np.random.default_rng(160)
     batch, nkv, s_max, hd, bs = 3, 2, 200, 128, 32
