@@ -212,3 +212,64 @@ def test_timer_validation():
     L = B.lib()
     assert L.llama_layer_timer_start(-1, 4) == -1
     assert L.llama_layer_timer_start(0, 0) == -1
+
+
+def paged_decode_rc(c, table=FAKE + 0x700000, n_blocks=8, block_size=16, max_blocks=2, ctx=FAKE + 0x600000,
+                    batch=2, max_ctx=10, ws_bytes=1, kp=FAKE + 0x300000):
+    w = weights()
+    return B.lib().llama_layer_decode_paged(ctypes.byref(c), ctypes.byref(w.struct), FAKE + 0x100000,
+                                            FAKE + 0x200000, kp, FAKE + 0x400000, n_blocks,
+                                            block_size, table, max_blocks, ctx, batch, max_ctx,
+                                            FAKE + 0x500000, ws_bytes, None)
+
+
+def paged_prefill_rc(c, table=FAKE + 0x700000, n_blocks=8, block_size=16, max_blocks=2, tokens=8,
+                     start_pos=0, ws_bytes=1):
+    w = weights()
+    return B.lib().llama_layer_prefill_paged(ctypes.byref(c), ctypes.byref(w.struct),
+                                             FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
+                                             FAKE + 0x400000, n_blocks, block_size, table,
+                                             max_blocks, 1, tokens, start_pos, FAKE + 0x500000,
+                                             ws_bytes, None)
+
+
+def test_paged_validation():
+    c = cfg()
+    assert paged_decode_rc(c) == -5                      # everything valid up to the workspace
+    assert paged_decode_rc(c, table=None) == -2
+    assert paged_decode_rc(c, table=FAKE + 0x700002) == -3
+    assert paged_decode_rc(c, kp=FAKE + 0x300008) == -3
+    assert paged_decode_rc(c, block_size=24) == -1       # not a power of two
+    assert paged_decode_rc(c, block_size=8) == -1        # below 16
+    assert paged_decode_rc(c, block_size=2048) == -1     # above 1024
+    assert paged_decode_rc(c, n_blocks=0) == -1
+    assert paged_decode_rc(c, max_blocks=0) == -1
+    assert paged_decode_rc(c, max_ctx=32) == -4          # 2 blocks of 16: position 32 is past
+    assert paged_decode_rc(c, max_ctx=31) == -5
+    assert paged_decode_rc(c, batch=0) == -1
+    assert paged_prefill_rc(c) == -5
+    assert paged_prefill_rc(c, table=None) == -2
+    assert paged_prefill_rc(c, block_size=12) == -1
+    assert paged_prefill_rc(c, start_pos=30, tokens=3) == -4
+    assert paged_prefill_rc(c, start_pos=24, tokens=8) == -5
+
+
+def test_w8_decode_validation():
+    c = cfg()
+    names = [n for n, _ in B.ll_weights_w8._fields_]
+    ptrs = {n: FAKE + 256 * i for i, n in enumerate(names)}
+
+    def rc(c=c, **kw):
+        p = dict(ptrs)
+        p.update(kw)
+        w = B.ll_weights_w8(*[p[n] for n in names])
+        return B.lib().llama_layer_decode_w8(ctypes.byref(c), ctypes.byref(w), FAKE + 0x100000,
+                                             FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                             FAKE + 0x600000, 2, 10, 32, FAKE + 0x500000, 1, None)
+    assert rc() == -5
+    assert rc(w_down=None) == -2
+    assert rc(s_gate=None) == -2
+    assert rc(s_up=FAKE + 2) == -3
+    assert rc(c=cfg(intermediate=680)) == -1             # not a multiple of 16
+    assert B.lib().llama_layer_decode_w8(ctypes.byref(c), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1,
+                                         32, FAKE, 1, None) == -2
