@@ -336,7 +336,7 @@ def main():
                     choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
                              "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8",
                              "sample_b32_v32000", "decode_7b_b1_ctx4096_w8",
-                             "decode_70b_b32_ragged_paged"])
+                             "decode_70b_b32_ragged_paged", "decode_70b_b32_ragged_w8"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)

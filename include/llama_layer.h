@@ -227,10 +227,11 @@ typedef struct ll_weights_w8 {
  * llama_layer_decode with INT8 weights: the same arguments, workspace size
  * (llama_layer_workspace_size with tokens = 1), caches and results, the
  * projections reading one byte per weight.  Sequences go through in groups
- * of up to 4 (fewer when 4 rows of the longest reduction would not fit the
- * 128 KB activation stage), each group reading every weight once, so the
- * entry point is meant for batches of 1 to 4.  hidden, intermediate and
- * n_heads * head_dim must be multiples of 16.
+ * that read every weight once: up to 32 with bf16/f16 activations when
+ * hidden, intermediate and n_heads * head_dim are multiples of 64, else up
+ * to 4 (fewer when 4 rows of the longest reduction would not fit the 128 KB
+ * activation stage).  hidden, intermediate and n_heads * head_dim must be
+ * multiples of 16.
  * Errors: as llama_layer_decode; LL_EUNSUPPORTED when a single row of the
  * longest reduction does not fit the stage.
  */

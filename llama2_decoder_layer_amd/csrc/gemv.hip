@@ -586,7 +586,10 @@ bool gemv_w8_fits(int dt, int M, int K) {
 }
 
 hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s) {
-  if (!gemv_w8_fits(dt, a.M, a.K) || !a.wscale[0]) return hipErrorInvalidValue;
+  if (!a.wscale[0]) return hipErrorInvalidValue;
+  // More tokens (or a stage that does not fit) go through the LDS-streaming
+  // kernel, which reads every weight once for up to 32 tokens.
+  if (!gemv_w8_fits(dt, a.M, a.K)) return launch_gemv_dma_w8(dt, epi, a, s);
   switch (dt) {
     case DT_F32: return gemv_w8_dt<DT_F32>(epi, a, s);
     case DT_BF16: return gemv_w8_dt<DT_BF16>(epi, a, s);

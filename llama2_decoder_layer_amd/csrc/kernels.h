@@ -79,6 +79,9 @@ bool gemv_fits_lds(int dt, int M, int K);
 constexpr int GEMV_W8_LDS_BYTES = 128 * 1024;
 bool gemv_w8_fits(int dt, int M, int K);
 hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
+// Weight-only int8 through the LDS-streaming kernel (16-bit activations, M <= 32,
+// K % 64 == 0, no fused norm; partials as gemv_dma_partial_floats).
+hipError_t launch_gemv_dma_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
 // Positions [start, start + count) of every (sequence, KV head) of contiguous
 // caches [B, nkv, s_max, hd] copied into the pools of a paged cache.
 hipError_t launch_kv_pages_write(const void* k_src, const void* v_src, int s_max, int start,

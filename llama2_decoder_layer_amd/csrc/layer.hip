@@ -212,7 +212,7 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
 
   // RMSNorm is fused into the projection when the m activation rows fit its
   // LDS stage; otherwise a norm pass writes u first.
-  const bool fuse_norm = w8 ? true : gemv_fits_lds(dt, m, H);
+  const bool fuse_norm = w8 ? gemv_w8_fits(dt, m, H) : gemv_fits_lds(dt, m, H);
   void* u = ws + L.u;
   const void* attn_norm = w8 ? w8->attn_norm : w->attn_norm;
   const void* ffn_norm = w8 ? w8->ffn_norm : w->ffn_norm;
@@ -590,10 +590,15 @@ int llama_quantize_w8(const void* w, int8_t* q, float* scale, int32_t rows, int3
   return LL_OK;
 }
 
-// Tokens per launch group of the int8 decode: at most 4 (the row kernel),
-// fewer when the activations of the longest K would not fit its LDS stage.
+// Tokens per launch group of the int8 decode: 32 through the LDS-streaming
+// kernel (16-bit activations, reductions a multiple of 64); else at most 4
+// (the row kernel), fewer when the activations of the longest K would not
+// fit its LDS stage.
 static int w8_group(const ll_config* c) {
-  const int kmax = std::max(std::max(c->hidden, c->intermediate), c->n_heads * c->head_dim);
+  const int qd = c->n_heads * c->head_dim;
+  if (c->act_dtype != LL_F32 && c->hidden % 64 == 0 && c->intermediate % 64 == 0 && qd % 64 == 0)
+    return 32;
+  const int kmax = std::max(std::max(c->hidden, c->intermediate), qd);
   int g = 4;
   while (g > 0 && !gemv_w8_fits(c->act_dtype, g, kmax)) --g;
   return g;

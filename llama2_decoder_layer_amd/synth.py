@@ -139,6 +139,11 @@ WORKLOADS = {
     "decode_70b_b32_ragged_paged": Workload("decode_70b_b32_ragged_paged", 3, L70B, "bf16", "f16",
                                             "decode", batch=32, ctx_range=(512, 4096), s_max=4097,
                                             extra={"block_size": 64}),
+    # The 70B batch-32 decode with INT8 projections (same weights, input and
+    # lengths as the bf16 workload: seed index 3).
+    "decode_70b_b32_ragged_w8": Workload("decode_70b_b32_ragged_w8", 3, L70B, "bf16", "f16",
+                                         "decode", batch=32, ctx_range=(512, 4096), s_max=4097,
+                                         extra={"w8": True}),
     # The 7B decode with weight-only INT8 projections (codes and scales made
     # on the device from the bf16 weights).
     "decode_7b_b1_ctx4096_w8": Workload("decode_7b_b1_ctx4096_w8", 7, L7B, "bf16", "bf16",

@@ -129,6 +129,23 @@ def test_w8_decode_large_activation_stage():
                   143)
 
 
+def test_w8_decode_streaming_ragged():
+    # 24 sequences in one group through the int8 LDS-streaming kernel; K = 576
+    # and 1152 end in a partial 256-k stage, f16 cache, GQA 4:1
+    ctx = list(np.random.default_rng(8).integers(0, 700, 24))
+    run_w8_decode("w8-stream", S.Shape(576, 8, 2, 64, 1152), "bf16", "f16", ctx, 800, 144)
+
+
+def test_w8_decode_70b_b32_full():
+    """The batched INT8 benchmark case: the 70B GQA layer at batch 32."""
+    name = "decode_70b_b32_ragged_w8"
+    wl = S.WORKLOADS[name]
+    say(f"[{name}] drawing inputs")
+    stored, inp = S.workload_layer_and_inputs(name)
+    run_w8_decode(name, wl.shape, wl.act_dtype, wl.kv_dtype, list(inp["ctx_len"]), wl.s_max, 0,
+                  stored=stored, inp=inp)
+
+
 def test_w8_decode_7b_full():
     """The INT8 benchmark case: the 7B layer at context 4096."""
     name = "decode_7b_b1_ctx4096_w8"
