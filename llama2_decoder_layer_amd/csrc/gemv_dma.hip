@@ -36,9 +36,11 @@ constexpr int SK_MAX_SPLIT = 8;
 // Features covered by one workgroup and the number of K splits used.
 static int sk_features(int epi) { return epi == EPI_SWIGLU ? SK_BM / 2 : SK_BM; }
 
-static int sk_split(int epi, int N, int K, int* kchunk) {
-  const int nblk = (N + sk_features(epi) - 1) / sk_features(epi);
-  int ns = (SK_TARGET_WG + nblk - 1) / nblk;
+// Splits of K for a launch whose workgroups cover `feats` features each, to
+// reach about `target` workgroups.
+static int sk_split_f(int feats, int N, int K, int* kchunk, int target = SK_TARGET_WG) {
+  const int nblk = (N + feats - 1) / feats;
+  int ns = (target + nblk - 1) / nblk;
   ns = std::max(1, std::min(ns, SK_MAX_SPLIT));
   const int nkt = K / 64;
   ns = std::min(ns, nkt);
@@ -46,6 +48,16 @@ static int sk_split(int epi, int N, int K, int* kchunk) {
   *kchunk = kt_per * 64;
   return (nkt + kt_per - 1) / kt_per;
 }
+
+static int sk_split(int epi, int N, int K, int* kchunk) {
+  return sk_split_f(sk_features(epi), N, K, kchunk);
+}
+
+// Code rows per workgroup of the int8 streaming kernel, its features, and the
+// workgroups wanted per launch (one per CU at 144 KB of LDS).
+constexpr int W8_BMW = 128;
+constexpr int W8_TARGET_WG = 256;
+static int w8_features(int epi) { return epi == EPI_SWIGLU ? W8_BMW / 2 : W8_BMW; }
 
 // Weight rows of a launch: N (SwiGLU: gate rows then up rows, 2N).
 static int sk_rows(int epi, int N) { return epi == EPI_SWIGLU ? 2 * N : N; }
@@ -275,48 +287,65 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   }
 }
 
-// Weight-only int8 variant: 64 rows of int8 codes (256-byte slices of a 256-k
-// stage, 16 KB) and the token slots (512-byte slices, 16 KB) stream through
-// LDS four stages deep.  The A fragment of a k-step is 8 codes (8 bytes),
+// Weight-only int8 variant: rows of int8 codes (256-byte slices of a 256-k
+// stage) and the token slots (512-byte slices, 16 KB) stream through LDS.
+// The A fragment of a k-step is 8 codes (8 bytes),
 // converted to the activation format (exact: |code| <= 127) before the MFMA;
 // each row's float32 scale multiplies its sums after the k loop, so partials
 // and results carry code x activation x scale as the row kernel computes.
 // The 16-byte chunks of a weight slice are swizzled by (row & 15) like the
 // activation slices; the 8-byte fragment reads then see 2-way bank conflicts.
-// Eight waves (two row blocks x four k slices of each stage, their fragment
-// reads issued before the conversions): at the 70B batch-32 decode gate/up
-// took 153 us with four waves and the k-steps one after another, 143 us with
-// the reads batched, 127 us with eight waves; sixteen measured the same.
+// Eight waves with the stage's fragment reads issued before the conversions,
+// 128 code rows per workgroup (4 row blocks x 2 k halves; 48 KB stages three
+// deep, so a CU has 64 KB of codes in flight) and about one workgroup per CU
+// per launch: at the 70B batch-32 decode gate/up took 153 us with four waves,
+// 64 rows and the k-steps one after another, 143 us with the reads batched,
+// 127 us with eight waves (sixteen: the same), 106 us with 128 rows and no K
+// split (the step 381 -> 301 us).
 constexpr int W8_BK = 256;
-constexpr int W8_NST = 4;
-constexpr int W8_WROWB = W8_BK;                  // bytes of a weight row slice
-constexpr int W8_AROWB = W8_BK * 2;              // bytes of a token row slice
-constexpr int W8_WBYTES = SK_BM * W8_WROWB;      // 16 KB
-constexpr int W8_STAGE = W8_WBYTES + SK_BN * W8_AROWB;  // 32 KB
-constexpr int W8_NW = 8;                         // waves: 2 row blocks x W8_NW/2 k slices
-constexpr int W8_NIW = W8_STAGE / 1024 / W8_NW;  // DMA instructions per wave and stage
-constexpr int W8_NIW_W = W8_WBYTES / 1024 / W8_NW;  // of them weights
-constexpr int W8_KS2 = W8_BK / 16 / (W8_NW / 2);  // k-steps per wave and stage
+constexpr int W8_NW = 8;                         // waves per workgroup
 
-// Scale of row r (0..63) of the workgroup's block.
-__device__ __forceinline__ float w8_row_scale(const ProjArgs& a, bool swi, int f0, int r) {
+// Geometry for BMW code rows per workgroup: RB row blocks of 32 x KSL k
+// slices of each stage over the eight waves; NST stages of codes (BMW x 256
+// bytes) and token slots (32 x 512 bytes).
+template <int BMW>
+struct W8Geom {
+  static_assert(BMW == 64 || BMW == 128, "rows per workgroup");
+  static constexpr int RB = BMW / 32;
+  static constexpr int KSL = W8_NW / RB;
+  static constexpr int KS2 = W8_BK / 16 / KSL;   // k-steps per wave and stage
+  static constexpr int NST = BMW == 64 ? 4 : 3;
+  static constexpr int WBYTES = BMW * W8_BK;
+  static constexpr int ABYTES = SK_BN * W8_BK * 2;
+  static constexpr int STAGE = WBYTES + ABYTES;
+  static constexpr int NIW = STAGE / 1024 / W8_NW;    // DMA instructions per wave and stage
+  static constexpr int NIW_W = WBYTES / 1024 / W8_NW;  // of them codes
+  static constexpr int LDS = NST * STAGE;
+  static_assert((KSL - 1) * RB * 64 * 64 <= LDS, "the k-slice sums reuse the ring");
+};
+
+// Scale of row r of the workgroup's block (SwiGLU: gate rows, then up rows).
+__device__ __forceinline__ float w8_row_scale(const ProjArgs& a, int half, bool swi, int f0,
+                                              int r) {
   if (swi) {
-    const int f = f0 + (r & 31);
-    return a.wscale[r < 32 ? 0 : 1][f < a.N ? f : 0];
+    const int f = f0 + (r < half ? r : r - half);
+    return a.wscale[r < half ? 0 : 1][f < a.N ? f : 0];
   }
   int f = f0 + r;
   f = f < a.N ? f : 0;
   return f < a.seg1 ? a.wscale[0][f] : f < a.seg2 ? a.wscale[1][f - a.seg1] : a.wscale[2][f - a.seg2];
 }
 
-template <int DT, int EPI, bool SPLIT>
+template <int DT, int EPI, bool SPLIT, int BMW>
 __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, float* part,
                                                                   int kchunk, int nsplit) {
   typedef typename Elt<DT>::T T;
+  typedef W8Geom<BMW> G;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
-  constexpr int FB = SWI ? SK_BM / 2 : SK_BM;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[W8_NST * W8_STAGE];
-  f32x16* red = reinterpret_cast<f32x16*>(lds);  // [W8_NW/2 - 1][2][64] after the k loop
+  constexpr int HALF = BMW / 2;
+  constexpr int FB = SWI ? HALF : BMW;  // features per workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS];
+  f32x16* red = reinterpret_cast<f32x16*>(lds);  // [KSL-1][RB][64] after the k loop
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = a.K;
@@ -326,23 +355,24 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
   const int klen = min(K, k0 + kchunk) - k0;  // a multiple of 64
   const int nkt = (klen + W8_BK - 1) / W8_BK;
 
-  // DMA: wave w issues instructions i = w + 8j.  i < 16: weight rows 4i + l/16,
-  // physical chunk l%16 (16 codes); else token rows 2(i-16) + l/32, physical
-  // chunk l%32 (8 elements).  Logical chunk = physical ^ (row & 15).  Chunks
-  // past the K range re-read the range's first one (their k-steps are skipped).
-  const uint8_t* src[W8_NIW];
-  int kofs[W8_NIW];  // element (= byte for codes) offset of the chunk in a stage
-  int esz[W8_NIW];
+  // DMA: wave w issues instructions i = w + 8j.  i < BMW/4: code rows 4i + l/16,
+  // physical chunk l%16 (16 codes); else token rows 2(i - BMW/4) + l/32,
+  // physical chunk l%32 (8 elements).  Logical chunk = physical ^ (row & 15).
+  // Chunks past the K range re-read the range's first one (their k-steps are
+  // skipped), so every wave issues the same number of loads per stage.
+  const uint8_t* src[G::NIW];
+  int kofs[G::NIW];  // element (= byte for codes) offset of the chunk in a stage
+  int esz[G::NIW];
 #pragma unroll
-  for (int j = 0; j < W8_NIW; ++j) {
+  for (int j = 0; j < G::NIW; ++j) {
     const int i = wave + W8_NW * j;
-    if (j < W8_NIW_W) {
+    if (j < G::NIW_W) {
       const int r = 4 * i + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
       const int8_t* row;
       if constexpr (SWI) {
-        const int f = f0 + (r & 31);
-        row = reinterpret_cast<const int8_t*>(r < 32 ? a.w[0] : a.w[1]) + (size_t)(f < a.N ? f : 0) * K;
+        const int f = f0 + (r < HALF ? r : r - HALF);
+        row = reinterpret_cast<const int8_t*>(r < HALF ? a.w[0] : a.w[1]) + (size_t)(f < a.N ? f : 0) * K;
       } else {
         const int f = f0 + r;
         row = seg_row<int8_t>(a, f < a.N ? f : 0);
@@ -351,7 +381,7 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
       kofs[j] = c * 16;
       esz[j] = 1;
     } else {
-      const int m = 2 * (i - 16) + (lane >> 5);
+      const int m = 2 * (i - BMW / 4) + (lane >> 5);
       const int c = (lane & 31) ^ (m & 15);
       const T* row = reinterpret_cast<const T*>(a.x) + (size_t)(m < a.M ? m : 0) * K;
       src[j] = reinterpret_cast<const uint8_t*>(row + k0);
@@ -360,28 +390,28 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
     }
   }
   auto issue = [&](int st, int kt) {
-    uint8_t* base = lds + st * W8_STAGE;
+    uint8_t* base = lds + st * G::STAGE;
     const int k = kt * W8_BK;
 #pragma unroll
-    for (int j = 0; j < W8_NIW; ++j) {
+    for (int j = 0; j < G::NIW; ++j) {
       const int kk = k + kofs[j];
       const uint8_t* g = src[j] + (size_t)(kk < klen ? kk : 0) * esz[j];
       uint8_t* d = base + (wave + W8_NW * j) * 1024;
-      if (j < W8_NIW_W) dma16_stream(g, d);
+      if (j < G::NIW_W) dma16_stream(g, d);
       else dma16(g, d);
     }
   };
   auto wait_stage = [&](int newer) {
-    static_for<0, W8_NST - 1>([&](auto n) {
-      if (newer == decltype(n)::value) wait_vmcnt<decltype(n)::value * W8_NIW>();
+    static_for<0, G::NST - 1>([&](auto n) {
+      if (newer == decltype(n)::value) wait_vmcnt<decltype(n)::value * G::NIW>();
     });
   };
 
-  const int rb = wave & 1, kh = wave >> 1;  // row block, k slice of each stage
+  const int rb = wave % G::RB, kh = wave / G::RB;  // row block, k slice of each stage
   const int l32 = lane & 31, h2 = lane >> 5;
   const int swz = l32 & 15;
-  const int aoff = (rb * 32 + l32) * W8_WROWB + 8 * h2;
-  const int boff = W8_WBYTES + l32 * W8_AROWB;
+  const int aoff = (rb * 32 + l32) * W8_BK + 8 * h2;
+  const int boff = G::WBYTES + l32 * W8_BK * 2;
 
   // 8 codes -> one fragment in the activation format.
   auto to_frag = [&](u32x2 raw) {
@@ -398,31 +428,31 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 
 #pragma unroll
-  for (int st = 0; st < W8_NST - 1; ++st)
+  for (int st = 0; st < G::NST - 1; ++st)
     if (st < nkt) issue(st, st);
   for (int kt = 0; kt < nkt; ++kt) {
-    wait_stage(min(nkt - 1, kt + W8_NST - 2) - kt);
+    wait_stage(min(nkt - 1, kt + G::NST - 2) - kt);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + W8_NST - 1 < nkt) issue((kt + W8_NST - 1) % W8_NST, kt + W8_NST - 1);
-    const uint8_t* base = lds + (kt % W8_NST) * W8_STAGE;
-    const int nvalid = (klen - kt * W8_BK) / 16 - kh * W8_KS2;
-    if (nvalid >= W8_KS2) {
+    if (kt + G::NST - 1 < nkt) issue((kt + G::NST - 1) % G::NST, kt + G::NST - 1);
+    const uint8_t* base = lds + (kt % G::NST) * G::STAGE;
+    const int nvalid = (klen - kt * W8_BK) / 16 - kh * G::KS2;
+    if (nvalid >= G::KS2) {
       // Every fragment read of the stage first, then conversions and MFMAs.
-      u32x2 raw[W8_KS2];
-      u32x4 bfr[W8_KS2];
+      u32x2 raw[G::KS2];
+      u32x4 bfr[G::KS2];
 #pragma unroll
-      for (int t = 0; t < W8_KS2; ++t) {
-        const int ks16 = kh * W8_KS2 + t;  // k-step: k = 16 ks16 .. +15
+      for (int t = 0; t < G::KS2; ++t) {
+        const int ks16 = kh * G::KS2 + t;  // k-step: k = 16 ks16 .. +15
         raw[t] = *reinterpret_cast<const u32x2*>(base + aoff + ((ks16 ^ swz) << 4));
         bfr[t] = ld16(base + boff + (((2 * ks16 + h2) ^ swz) << 4));
       }
 #pragma unroll
-      for (int t = 0; t < W8_KS2; ++t) acc = mfma32<DT>(to_frag(raw[t]), bfr[t], acc);
+      for (int t = 0; t < G::KS2; ++t) acc = mfma32<DT>(to_frag(raw[t]), bfr[t], acc);
     } else {
       for (int t = 0; t < nvalid; ++t) {
-        const int ks16 = kh * W8_KS2 + t;
+        const int ks16 = kh * G::KS2 + t;
         const u32x2 r = *reinterpret_cast<const u32x2*>(base + aoff + ((ks16 ^ swz) << 4));
         const u32x4 b = ld16(base + boff + (((2 * ks16 + h2) ^ swz) << 4));
         acc = mfma32<DT>(to_frag(r), b, acc);
@@ -431,26 +461,27 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // k slices meet: waves with kh > 0 hand their sums to the kh = 0 pair.
+  // k slices meet: waves with kh > 0 hand their sums to the kh = 0 waves,
+  // which apply the row scales (lane: rows rb*32 + g*8 + h2*4 + i).  Every
+  // wave passes every barrier before any returns.
   __syncthreads();
-  if (kh > 0) red[((kh - 1) * 2 + rb) * 64 + lane] = acc;
+  if (kh > 0) red[((kh - 1) * G::RB + rb) * 64 + lane] = acc;
   __syncthreads();
   if (kh == 0) {
 #pragma unroll
-    for (int q = 0; q < W8_NW / 2 - 1; ++q) acc += red[(q * 2 + rb) * 64 + lane];
-  }
-  // Row scales: lane holds rows rb*32 + g*8 + h2*4 + i.
-  if (kh == 0) {
+    for (int q = 0; q < G::KSL - 1; ++q) acc += red[(q * G::RB + rb) * 64 + lane];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[g * 4 + i] *= w8_row_scale(a, SWI, f0, rb * 32 + g * 8 + h2 * 4 + i);
+      for (int i = 0; i < 4; ++i)
+        acc[g * 4 + i] *= w8_row_scale(a, HALF, SWI, f0, rb * 32 + g * 8 + h2 * 4 + i);
   }
   if constexpr (!SPLIT && SWI) {
+    // Gate rows are in row blocks 0 .. RB/2 - 1, the matching up rows RB/2 later.
+    __syncthreads();  // every read of red is done
+    if (kh == 0 && rb >= G::RB / 2) red[(rb - G::RB / 2) * 64 + lane] = acc;
     __syncthreads();
-    if (wave == 1) red[lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
+    if (rb >= G::RB / 2) return;
   }
   if (kh > 0) return;
 
@@ -462,8 +493,8 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r = rb * 32 + g * 8 + h2 * 4;
-        const int f = SWI ? (r < 32 ? f0 + r : a.N + f0 + r - 32) : f0 + r;
-        if ((SWI ? f0 + (r & 31) : f) < a.N) {
+        const int f = SWI ? (r < HALF ? f0 + r : a.N + f0 + r - HALF) : f0 + r;
+        if ((SWI ? f0 + (r < HALF ? r : r - HALF) : f) < a.N) {
           f32x4 v = {acc[g * 4], acc[g * 4 + 1], acc[g * 4 + 2], acc[g * 4 + 3]};
           *reinterpret_cast<f32x4*>(p + f) = v;
         }
@@ -471,10 +502,10 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
     }
   } else if constexpr (SWI) {
     if (m >= a.M) return;
-    const f32x16 up = red[lane];
+    const f32x16 up = red[rb * 64 + lane];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int f = f0 + g * 8 + h2 * 4;
+      const int f = f0 + rb * 32 + g * 8 + h2 * 4;
       if (f >= a.N) continue;
       float v[4], u[4];
 #pragma unroll
@@ -518,7 +549,9 @@ __global__ __launch_bounds__(256) void gemv_split_reduce_kernel(ProjArgs a, cons
 size_t gemv_dma_partial_floats(int epi, int N, int K, int M) {
   if (K % 64 != 0 || M < 1 || M > SK_BN) return 0;
   int kchunk;
-  const int ns = sk_split(epi, N, K, &kchunk);
+  // Room for the splits of the 16-bit kernel and of the int8 one.
+  const int ns = std::max(sk_split(epi, N, K, &kchunk),
+                          sk_split_f(w8_features(epi), N, K, &kchunk, W8_TARGET_WG));
   return ns > 1 ? (size_t)ns * M * sk_rows(epi, N) : 0;
 }
 
@@ -553,16 +586,16 @@ static hipError_t gemv_dma_epi(const ProjArgs& a, hipStream_t s) {
 template <int DT, int EPI>
 static hipError_t gemv_dma_w8_epi(const ProjArgs& a, hipStream_t s) {
   int kchunk;
-  const int ns = sk_split(EPI, a.N, a.K, &kchunk);
-  const int nblk = (a.N + sk_features(EPI) - 1) / sk_features(EPI);
+  const int ns = sk_split_f(w8_features(EPI), a.N, a.K, &kchunk, W8_TARGET_WG);
+  const int nblk = (a.N + w8_features(EPI) - 1) / w8_features(EPI);
   if (ns == 1) {
-    LL_LAUNCH((gemv_dma_w8_kernel<DT, EPI, false>), dim3(nblk), dim3(W8_NW * 64), 0, s, a,
+    LL_LAUNCH((gemv_dma_w8_kernel<DT, EPI, false, W8_BMW>), dim3(nblk), dim3(W8_NW * 64), 0, s, a,
               (float*)nullptr, kchunk, 1);
     return hipGetLastError();
   }
   if (!a.part) return hipErrorInvalidValue;
-  LL_LAUNCH((gemv_dma_w8_kernel<DT, EPI, true>), dim3(nblk * ns), dim3(W8_NW * 64), 0, s, a,
-            a.part, kchunk, ns);
+  LL_LAUNCH((gemv_dma_w8_kernel<DT, EPI, true, W8_BMW>), dim3(nblk * ns), dim3(W8_NW * 64), 0, s,
+            a, a.part, kchunk, ns);
   const int n = ((a.N + 3) / 4) * a.M;
   LL_LAUNCH((gemv_split_reduce_kernel<DT, EPI>), dim3((n + 255) / 256), dim3(256), 0, s, a,
             (const float*)a.part, ns);
