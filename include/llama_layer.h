@@ -19,6 +19,11 @@
  * sharing one K/V head); "LLM架构全景解析：从基础模块到工程实践" §2.2 (the cache
  * object written at the current position).
  *
+ * Around the layer: the same layer over a paged KV cache (decode and chunked
+ * prefill), with weight-only INT8 projections (decode), RoPE tables (also
+ * NTK-scaled for longer contexts), embedding lookup, the LM head with a
+ * greedy pick, and a fused sampler (penalty, temperature, top-k, top-p).
+ *
  * Conventions shared by every entry point
  *  - All tensor arguments are DEVICE pointers unless stated otherwise, dense,
  *    row-major, 16-byte aligned (int32 id/length arrays and float32 logits:
