@@ -24,6 +24,28 @@ constexpr int VT_STRIDE = PKV + 4;  // padded row of the transposed V tile (elem
 // CU; three or four (one workgroup per CU) measured 1.6-1.8x slower.
 constexpr int PF_STAGES = 2;
 
+// The work item (query block, head, sequence) of this workgroup; grid
+// (query blocks, heads, sequences).  Workgroup i of a launch runs on XCD
+// i % 8.  When the (sequence, head) units split evenly over the 8 XCDs, each
+// XCD takes a contiguous run of units, so the query blocks of a head (and the
+// heads of one KV group) read their K and V through one L2, and walks its
+// units heaviest (latest) query block first.  Otherwise the grid order, also
+// heaviest first.
+struct PrefillItem {
+  int qb, h, b;
+};
+__device__ __forceinline__ PrefillItem prefill_item() {
+  const int nqb = gridDim.x, nh = gridDim.y;
+  const int units = nh * gridDim.z;
+  if (units % 8 != 0) return {nqb - 1 - (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+  const int lin = blockIdx.x + nqb * (blockIdx.y + nh * blockIdx.z);
+  const int xcd = lin & 7, r = lin >> 3;  // r < nqb * units / 8
+  const int per = units / 8;
+  const int qi = r / per;
+  const int u = xcd * per + (r - qi * per);
+  return {nqb - 1 - qi, u % nh, u / nh};
+}
+
 template <int DT, int HD>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   typedef typename Elt<DT>::T ET;
@@ -39,10 +61,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
-  const int nqb = gridDim.x;
-  const int qb = nqb - 1 - blockIdx.x;  // heavy blocks first
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const PrefillItem it = prefill_item();
+  const int qb = it.qb, h = it.h, b = it.b;
   const int j = h / (a.nh / a.nkv);
   const int T = a.T;
 
@@ -237,10 +257,8 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
-  const int nqb = gridDim.x;
-  const int qb = nqb - 1 - blockIdx.x;  // heavy blocks first
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const PrefillItem it = prefill_item();
+  const int qb = it.qb, h = it.h, b = it.b;
   const int j = h / (a.nh / a.nkv);
   const int T = a.T;
 
