@@ -328,6 +328,36 @@ def dequantize_w8(codes, scales) -> np.ndarray:
     return np.asarray(codes, dtype=F64) * np.asarray(scales, dtype=F64)[:, None]
 
 
+def quantize_w4_rows(w):
+    """Weight-only INT4 by rows ("Llama2架构与推理全解析" §3.2: about half a byte
+    per weight, so a 7B model in roughly 4 GB, at a larger loss of precision
+    than INT8).
+
+    Reading: the INT8 scheme with 4-bit codes.  Symmetric round-to-nearest per
+    output row, the scale being the row's largest magnitude over 7; codes =
+    rint(w / scale) clipped to [-7, 7] (ties to even); an all-zero row gets
+    scale 0 and codes 0.  Scale and division in float32, as for INT8.  How the
+    codes are packed two to a byte is a storage layout, not part of this
+    definition.
+
+    w: [rows, cols] (values exactly representable in float32).
+    Returns (codes int8 [rows, cols] in [-7, 7], scales float32 [rows]).
+    """
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=1)
+    scale = (amax / np.float32(7.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint(w32 / safe[:, None])
+    q = np.where(scale[:, None] > 0, np.clip(q, -7, 7), 0)
+    return q.astype(np.int8), scale
+
+
+def dequantize_w4(codes, scales) -> np.ndarray:
+    """The weights an INT4 layer computes with: codes times the row scale, in
+    float64 (exact)."""
+    return np.asarray(codes, dtype=F64) * np.asarray(scales, dtype=F64)[:, None]
+
+
 def sampling_distribution(logits, history, temperature: float, top_k: int, top_p: float,
                           penalty: float):
     """The distribution one token is drawn from ("Llama2架构与推理全解析" §2.5;

@@ -500,6 +500,35 @@ def check_quantize_w8():
     assert abs(sc[0] - 0.01) < 1e-9 and list(q[0]) == [127, -64, 2, 1, -127]
 
 
+def check_quantize_w4():
+    """The same properties with 4-bit codes: every weight within half a step,
+    each row's largest magnitude on +-7, odd symmetry, dequantised rows
+    quantise back to themselves, a zero row stays zero, and a hand-worked row."""
+    r = _rng(31)
+    w = (r.standard_normal((64, 300)) * 0.02).astype(np.float32)
+    w[5] = 0.0
+    w[7, :] = 0.0
+    w[7, 3] = 0.5
+    q, sc = R.quantize_w4_rows(w)
+    assert q.dtype == np.int8 and sc.dtype == np.float32
+    assert np.all(np.abs(q.astype(int)) <= 7)
+    err = np.abs(w.astype(np.float64) - R.dequantize_w4(q, sc))
+    assert np.all(err <= sc.astype(np.float64)[:, None] * (0.5 + 1e-6))
+    nz = sc > 0
+    assert np.all(np.max(np.abs(q[nz].astype(int)), axis=1) == 7)
+    assert sc[5] == 0 and not np.any(q[5])
+    assert q[7, 3] == 7 and np.count_nonzero(q[7]) == 1
+    qn, scn = R.quantize_w4_rows(-w)
+    assert np.array_equal(qn, -q) and np.array_equal(scn, sc)
+    back = R.dequantize_w4(q, sc).astype(np.float32)
+    q2, sc2 = R.quantize_w4_rows(back)
+    assert np.array_equal(q2, q) and np.allclose(sc2, sc, rtol=1e-6, atol=0)
+    # by hand: max 0.7 -> scale 0.1; -0.33 -> -3.3 -> -3, 0.26 -> 2.6 -> 3,
+    # 0.04 -> 0.4 -> 0, 0.68 -> 6.8 -> 7
+    q, sc = R.quantize_w4_rows(np.array([[0.7, -0.33, 0.26, 0.04, 0.68, -0.7]], np.float32))
+    assert abs(sc[0] - 0.1) < 1e-8 and list(q[0]) == [7, -3, 3, 0, 7, -7]
+
+
 # --------------------------------------------------------------------------
 # Sampling
 # --------------------------------------------------------------------------
@@ -641,6 +670,6 @@ ALL_CHECKS = [
     check_gqa_reductions, check_silu_closed_forms, check_swiglu_special_cases,
     check_layer_transformers, check_layer_cached_decode_equals_recompute,
     check_layer_ragged_batch, check_greedy_ties, check_stack_cached_equals_recompute,
-    check_sizes_golden, check_quantize_w8, check_sampling_worked_example, check_sampling_inverse_cdf_counts,
+    check_sizes_golden, check_quantize_w8, check_quantize_w4, check_sampling_worked_example, check_sampling_inverse_cdf_counts,
     check_sampling_greedy_limits, check_sampling_transformers,
 ]

@@ -158,14 +158,14 @@ def _sample_index_order(logits, history, u, temperature, top_k, top_p, penalty):
     return out
 
 
-def _w8_generic(levels=127.0, rounding=np.rint, per_column=False):
+def _w8_generic(levels=127.0, rounding=np.rint, per_column=False, clip=127):
     def quant(w):
         w32 = np.asarray(w, dtype=np.float32)
         amax = np.max(np.abs(w32), axis=0 if per_column else 1)
         scale = (amax / np.float32(levels)).astype(np.float32)
         safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
         q = rounding(w32 / (safe[None, :] if per_column else safe[:, None]))
-        q = np.clip(q, -127, 127)
+        q = np.clip(q, -clip, clip)
         return q.astype(np.int8), (scale if not per_column else scale[:w32.shape[0]])
     return quant
 
@@ -191,6 +191,9 @@ MUTANTS = {
     "w8_scale_over_128": ("quantize_w8_rows", _w8_generic(levels=128.0)),
     "w8_truncates": ("quantize_w8_rows", _w8_generic(rounding=np.trunc)),
     "w8_column_scales": ("quantize_w8_rows", _w8_generic(per_column=True)),
+    "w4_scale_over_8": ("quantize_w4_rows", _w8_generic(levels=8.0, clip=7)),
+    "w4_truncates": ("quantize_w4_rows", _w8_generic(levels=7.0, rounding=np.trunc, clip=7)),
+    "w4_codes_to_8": ("quantize_w4_rows", _w8_generic(levels=7.5, clip=8)),
     "attention_no_scale": ("causal_gqa_attention", _attention_generic(scale="none")),
     "attention_scale_1_over_d": ("causal_gqa_attention", _attention_generic(scale="lin")),
     "attention_mask_excludes_self": ("causal_gqa_attention", _attention_generic(strict=True)),
