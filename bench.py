@@ -32,16 +32,17 @@ def layer_weight_elems(s) -> int:
     return (nh + 2 * nkv) * hd * H + H * nh * hd + 2 * I * H + H * I
 
 
-def decode_bytes(s, ctx_len, act_b, kv_b, w8=False) -> dict:
+def decode_bytes(s, ctx_len, act_b, kv_b, wbits=16) -> dict:
     """Algorithmic HBM bytes of one decode call: each weight once (INT8: one
-    byte per weight and a float32 scale per row), each cached K/V entry that is
-    attended once, the new K/V entries, x, y and the gains."""
+    byte per weight, INT4 half a byte, and a float32 scale per row), each
+    cached K/V entry that is attended once, the new K/V entries, x, y and the
+    gains."""
     B = len(ctx_len)
     kv_read = int(np.sum(np.asarray(ctx_len, np.int64) + 1)) * s.n_kv_heads * s.head_dim * 2 * kv_b
-    if w8:
+    if wbits in (8, 4):
         rows = (s.n_heads + 2 * s.n_kv_heads) * s.head_dim + s.hidden + 2 * s.intermediate + s.hidden
-        w = layer_weight_elems(s) + 4 * rows
-        gate_up = 2 * s.intermediate * s.hidden + 4 * 2 * s.intermediate
+        w = layer_weight_elems(s) * wbits // 8 + 4 * rows
+        gate_up = 2 * s.intermediate * s.hidden * wbits // 8 + 4 * 2 * s.intermediate
     else:
         w = layer_weight_elems(s) * act_b
         gate_up = 2 * s.intermediate * s.hidden * act_b
@@ -86,6 +87,9 @@ def cpu_baseline_decode(wl, stored, inp, budget_s: float) -> dict:
     if wl.extra.get("w8"):
         for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down"):
             w[k] = R.dequantize_w8(*R.quantize_w8_rows(w[k].astype(np.float32)))
+    if wl.extra.get("w4"):
+        for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down"):
+            w[k] = R.dequantize_w4(*R.quantize_w4_rows(w[k].astype(np.float32)))
     w = R.LayerWeights(**w)
     B = wl.batch
     nb = B if B <= 4 else 4  # bounded sample: the first sequences of the batch
@@ -336,7 +340,8 @@ def main():
                     choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
                              "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8",
                              "sample_b32_v32000", "decode_7b_b1_ctx4096_w8",
-                             "decode_70b_b32_ragged_paged", "decode_70b_b32_ragged_w8"])
+                             "decode_70b_b32_ragged_paged", "decode_70b_b32_ragged_w8",
+                             "decode_7b_b1_ctx4096_w4"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -374,7 +379,9 @@ def main():
             return torch.from_numpy(a).cuda()
         return torch.from_numpy(a.view(np.int16)).cuda().view(tdt[dt])
 
-    per_copy = layer_weight_elems(s) * (1 if wl.extra.get("w8") else act_b) + \
+    wbits = 8 if wl.extra.get("w8") else 4 if wl.extra.get("w4") else 16
+    per_copy = (layer_weight_elems(s) * wbits // 8 if wbits < 16 else
+                layer_weight_elems(s) * act_b) + \
         2 * inp["k_cache"].size * kv_b
     copies = args.copies or max(1, min(8, -(-1_500_000_000 // per_copy)))
     max_pos = wl.s_max
@@ -387,7 +394,7 @@ def main():
         B.llama_rope_table(rc, rs, max_pos, s.head_dim, s.rope_theta)
     else:
         B.llama_rope_table_ntk(rc, rs, max_pos, s.head_dim, s.rope_theta, ntk)
-    w8 = bool(wl.extra.get("w8"))
+    w8 = wbits == 8
     sets, tables = [], []
     for c in range(copies):
         w = {k: dev(v, act) for k, v in stored.items()}
@@ -401,6 +408,16 @@ def main():
                 w[k], w["s_" + k[2:]] = q, sc
             torch.cuda.synchronize()
             lw = B.LayerWeightsW8(w)
+        elif wbits == 4:
+            for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down"):
+                full = w.pop(k)
+                q = torch.empty(full.shape[0], full.shape[1] // 2, dtype=torch.uint8,
+                                device="cuda")
+                sc = torch.empty(full.shape[0], dtype=torch.float32, device="cuda")
+                B.llama_quantize_w4(full, q, sc, act)
+                w[k], w["s_" + k[2:]] = q, sc
+            torch.cuda.synchronize()
+            lw = B.LayerWeightsW4(w)
         else:
             lw = B.LayerWeights(w)
         if wl.extra.get("block_size"):
@@ -420,7 +437,8 @@ def main():
         ws = torch.empty(B.llama_layer_workspace_size(cfg, wl.batch, 1, s_ws), dtype=torch.uint8,
                          device="cuda")
 
-        run = B.llama_layer_decode_w8 if w8 else B.llama_layer_decode
+        run = {8: B.llama_layer_decode_w8, 4: B.llama_layer_decode_w4}.get(wbits,
+                                                                         B.llama_layer_decode)
         bs = wl.extra.get("block_size")
 
         def step(i):
@@ -431,7 +449,7 @@ def main():
             else:
                 run(cfg, lw, x, y, kc, vc, ctx, wl.batch, max_ctx, wl.s_max, ws)
         # the kernel moving the most bytes: gate/up, or attention at long contexts
-        by0 = decode_bytes(s, inp["ctx_len"], act_b, kv_b, w8)
+        by0 = decode_bytes(s, inp["ctx_len"], act_b, kv_b, wbits)
         dom = "attn_decode" if by0["attn_decode"] > by0["gemv_gate_up"] else "gemv_gate_up"
     else:
         x = dev(inp["x"], act)
@@ -477,7 +495,7 @@ def main():
     tr = load_traffic(dom, wl.name)
     traffic = None if tr is None else tr["bytes"]
     if decode:
-        by = decode_bytes(s, inp["ctx_len"], act_b, kv_b, bool(wl.extra.get("w8")))
+        by = decode_bytes(s, inp["ctx_len"], act_b, kv_b, wbits)
         out.update(value=wl.batch / (ms_step / 1e3), unit="tokens/s/layer")
         layer_gbps = by["total"] / (ms_step / 1e3) / 1e9
         out["layer_hbm"] = {"bytes_per_step": by["total"], "GBps": layer_gbps,
@@ -510,6 +528,8 @@ def main():
         out["config"]["rope_ntk_scale"] = wl.extra["ntk_scale"]
     if wl.extra.get("w8"):
         out["config"]["weights"] = "int8 codes, float32 scale per row"
+    if wl.extra.get("w4"):
+        out["config"]["weights"] = "int4 codes (two per byte), float32 scale per row"
     if wl.extra.get("block_size"):
         out["config"]["kv_cache"] = f"paged, {wl.extra['block_size']}-position blocks, shuffled pool"
     if args.no_cpu_baseline:

@@ -246,6 +246,53 @@ int llama_layer_decode_w8(const ll_config* cfg, const ll_weights_w8* w, const vo
                           void* stream);
 
 /*
+ * Weight-only INT4 ("Llama2架构与推理全解析" §3.2: about half a byte per
+ * weight, a 7B model in roughly 4 GB, at a larger loss of precision than
+ * INT8).  The INT8 scheme with 4-bit codes:
+ *   scale[r] = max_c |w[r, c]| / 7            (float32)
+ *   code     = rint(w[r, c] / scale[r])       (float32 division correctly
+ *              rounded, ties to even, in [-7, 7]; a zero row: scale 0, codes 0)
+ * packed two to a byte in two's complement nibbles: byte j of a row holds
+ * the code of column 2j in its low nibble and of column 2j + 1 in its high one.
+ *   w        DEVICE [rows, cols] in dtype, 16-byte aligned
+ *   q        DEVICE uint8 [rows, cols / 2], 16-byte aligned; scale DEVICE float32 [rows]
+ * Errors: LL_ENULL, LL_EALIGN, LL_EINVAL (rows or cols <= 0, cols % 32 != 0,
+ * bad dtype), LL_EHIP.
+ */
+int llama_quantize_w4(const void* w, uint8_t* q, float* scale, int32_t rows, int32_t cols,
+                      int32_t dtype, void* stream);
+
+/*
+ * A layer whose seven projection matrices are llama_quantize_w4 codes and
+ * scales (rows of cols / 2 bytes); the rest as in ll_weights_w8.  The layer
+ * computes with the weights code[r, c] * scale[r].
+ */
+typedef struct ll_weights_w4 {
+  const void* attn_norm;                       /* [hidden], act_dtype */
+  const uint8_t *w_q, *w_k, *w_v, *w_o;        /* [rows, cols / 2] packed codes */
+  const void* ffn_norm;                        /* [hidden], act_dtype */
+  const uint8_t *w_gate, *w_up, *w_down;
+  const float *s_q, *s_k, *s_v, *s_o;          /* float32, one per row of each */
+  const float *s_gate, *s_up, *s_down;
+  const float *rope_cos, *rope_sin;            /* float32 [max_pos, head_dim/2] */
+} ll_weights_w4;
+
+/*
+ * llama_layer_decode with INT4 weights: the same arguments, workspace size
+ * (llama_layer_workspace_size with tokens = 1), caches and results, the
+ * projections reading half a byte per weight.  Sequences go through in groups
+ * of up to 4 (fewer when 4 rows of the longest reduction would not fit the
+ * 128 KB activation stage), each group reading every weight once.  hidden,
+ * intermediate and n_heads * head_dim must be multiples of 32.
+ * Errors: as llama_layer_decode; LL_EUNSUPPORTED when a single row of the
+ * longest reduction does not fit the stage.
+ */
+int llama_layer_decode_w4(const ll_config* cfg, const ll_weights_w4* w, const void* x, void* y,
+                          void* k_cache, void* v_cache, const int32_t* ctx_len, int32_t batch,
+                          int32_t max_ctx, int32_t s_max, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
  * RoPE angle tables: cos/sin[m, i] = cos/sin(m * rope_theta^(-2i/head_dim)) for
  * m < max_pos, i < head_dim/2, evaluated in float64 on the device and rounded
  * to float32 ("Llama2架构与推理全解析" §1.4).  cos_out, sin_out: device float32

@@ -52,6 +52,10 @@ class ll_weights_w8(ctypes.Structure):
                  "rope_cos", "rope_sin")]
 
 
+class ll_weights_w4(ll_weights_w8):
+    """Same fields as ll_weights_w8; the w_* point to packed int4 rows."""
+
+
 _lib = None
 
 
@@ -92,6 +96,11 @@ def lib() -> ctypes.CDLL:
         L.llama_layer_decode_w8.argtypes = [CP, ctypes.POINTER(ll_weights_w8), P, P, P, P, P,
                                             I32, I32, I32, P, SZ, P]
         L.llama_layer_decode_w8.restype = ctypes.c_int
+        L.llama_quantize_w4.argtypes = [P, P, P, I32, I32, I32, P]
+        L.llama_quantize_w4.restype = ctypes.c_int
+        L.llama_layer_decode_w4.argtypes = [CP, ctypes.POINTER(ll_weights_w4), P, P, P, P, P,
+                                            I32, I32, I32, P, SZ, P]
+        L.llama_layer_decode_w4.restype = ctypes.c_int
         L.llama_embed.argtypes = [P, P, P, I32, I32, I32, I32, P]
         L.llama_embed.restype = ctypes.c_int
         L.llama_head_argmax.argtypes = [P, P, P, P, P, I32, I32, I32, F, I32, P]
@@ -187,6 +196,17 @@ class LayerWeightsW8:
         self.struct = ll_weights_w8(*[_ptr(self.tensors[n]) for n in self.NAMES])
 
 
+class LayerWeightsW4:
+    """Holds an INT4 layer's device tensors (packed codes, scales, norms, RoPE
+    tables) and their ll_weights_w4."""
+
+    NAMES = tuple(n for n, _ in ll_weights_w8._fields_)
+
+    def __init__(self, tensors: dict):
+        self.tensors = dict(tensors)
+        self.struct = ll_weights_w4(*[_ptr(self.tensors[n]) for n in self.NAMES])
+
+
 def llama_layer_decode_paged(cfg, weights: LayerWeights, x, y, k_pool, v_pool, block_size,
                              block_table, ctx_len, batch, max_ctx, ws, ws_bytes=None,
                              stream=None) -> None:
@@ -229,6 +249,23 @@ def llama_quantize_w8(w, q, scale, dtype, stream=None) -> None:
     rows, cols = w.shape
     _check(lib().llama_quantize_w8(_ptr(w), _ptr(q), _ptr(scale), rows, cols, DTYPE_CODE[dtype],
                                    _stream(stream)), "llama_quantize_w8")
+
+
+def llama_quantize_w4(w, q, scale, dtype, stream=None) -> None:
+    """w [rows, cols] device tensor stored in `dtype`; q uint8 [rows, cols/2]
+    (packed codes) and scale float32 outputs."""
+    rows, cols = w.shape
+    _check(lib().llama_quantize_w4(_ptr(w), _ptr(q), _ptr(scale), rows, cols, DTYPE_CODE[dtype],
+                                   _stream(stream)), "llama_quantize_w4")
+
+
+def llama_layer_decode_w4(cfg, weights: LayerWeightsW4, x, y, k_cache, v_cache, ctx_len, batch,
+                          max_ctx, s_max, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    rc = lib().llama_layer_decode_w4(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x),
+                                     _ptr(y), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), batch,
+                                     max_ctx, s_max, _ptr(ws), nbytes, _stream(stream))
+    _check(rc, "llama_layer_decode_w4")
 
 
 def llama_layer_decode_w8(cfg, weights: LayerWeightsW8, x, y, k_cache, v_cache, ctx_len, batch,

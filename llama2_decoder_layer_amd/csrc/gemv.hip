@@ -341,15 +341,18 @@ static hipError_t gemv_glb_launch(const ProjArgs& a, hipStream_t s) {
 // workgroup worth spreading over more rows) do that; O and down (4096 rows at
 // 7B) keep one row per wave, or half the CUs would sit idle, and with four
 // tokens the second row's registers spill.
+// W4 (with WQ): 4-bit codes instead, two per byte (weight 2j in the low
+// nibble of byte j), 32 per 16-byte load, sign-extended from the nibble.
 template <bool WQ, int MT, bool NORM>
 constexpr int row_rows_per_wave() { return (WQ && MT == 1 && NORM) ? 2 : 1; }
 
-template <int DT, int EPI, bool NORM, int MT, int NWV, bool WQ = false>
+template <int DT, int EPI, bool NORM, int MT, int NWV, bool WQ = false, bool W4 = false>
 __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
   typedef typename Elt<DT>::T T;
   typedef typename std::conditional<WQ, int8_t, T>::type TW;
+  static_assert(!W4 || WQ, "4-bit codes are a quantised format");
   constexpr int E = Elt<DT>::PER16;
-  constexpr int EW = WQ ? 16 : E;          // weights per 16-byte load
+  constexpr int EW = W4 ? 32 : WQ ? 16 : E;  // weights per 16-byte load
   constexpr int RPW = row_rows_per_wave<WQ, MT, NORM>();  // rows per wave
   constexpr int NS = NWV * RPW;            // row slots per workgroup
   constexpr bool SWI = (EPI == EPI_SWIGLU);
@@ -366,6 +369,7 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int K = a.K, M = a.M;
+  const int RS = W4 ? K / 2 : K;  // row stride in TW units
   const int f0 = blockIdx.x * FW;
   // Slot s (this wave's are wave, wave + NWV, ...): feature f0 + s (SwiGLU:
   // gate rows in the first FW slots, the matching up rows in the rest).  Rows
@@ -379,10 +383,16 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
     const int fs = f < a.N ? f : 0;
     wscale[r] = 1.f;
     if constexpr (SWI) {
-      wp[r] = reinterpret_cast<const TW*>(slot < FW ? a.w[0] : a.w[1]) + (size_t)fs * K;
+      wp[r] = reinterpret_cast<const TW*>(slot < FW ? a.w[0] : a.w[1]) + (size_t)fs * RS;
       if constexpr (WQ) wscale[r] = a.wscale[slot < FW ? 0 : 1][fs];
     } else {
-      wp[r] = seg_row<TW>(a, fs);
+      if constexpr (W4) {
+        const int sg = fs < a.seg1 ? 0 : fs < a.seg2 ? 1 : 2;
+        const int f_in = fs - (sg == 0 ? 0 : sg == 1 ? a.seg1 : a.seg2);
+        wp[r] = reinterpret_cast<const TW*>(a.w[sg]) + (size_t)f_in * RS;
+      } else {
+        wp[r] = seg_row<TW>(a, fs);
+      }
       if constexpr (WQ)
         wscale[r] = fs < a.seg1 ? a.wscale[0][fs]
                   : fs < a.seg2 ? a.wscale[1][fs - a.seg1] : a.wscale[2][fs - a.seg2];
@@ -396,7 +406,7 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
     for (int u = 0; u < U; ++u) {
       const int k = (c0 + u) * 64 * EW + lane * EW;
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) wv[r][u] = (k < K) ? ld16_stream(wp[r] + k) : zero;
+      for (int r = 0; r < RPW; ++r) wv[r][u] = (k < K) ? ld16_stream(wp[r] + (W4 ? k / 2 : k)) : zero;
     }
   };
   // Weight loads start before the activations are staged.
@@ -448,6 +458,35 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
     for (int u = 0; u < U; ++u) {
       const int k = (c0 + u) * 64 * EW + lane * EW;
       if (k >= K) break;
+      if constexpr (W4) {
+        // E activations at a time; their E codes come out of one or half a
+        // 32-bit word of each row.
+#pragma unroll
+        for (int h = 0; h < EW / E; ++h) {
+          float wf4[RPW][E];
+#pragma unroll
+          for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const int idx = h * E + e;
+              const uint32_t word = wv[r][u][idx >> 3];
+              wf4[r][e] = (float)((int32_t)(word << (28 - 4 * (idx & 7))) >> 28);
+            }
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            if (m < M) {
+              float xf[E];
+              unpack16<DT>(ld16(xs + (size_t)m * K + k + h * E), xf);
+#pragma unroll
+              for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[r][m] += wf4[r][e] * xf[e];
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
       float wf[RPW][EW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
@@ -543,8 +582,9 @@ static hipError_t gemv_row_launch(const ProjArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// int8 weights, 1-4 tokens: the row kernel with a larger activation stage.
-template <int DT, int EPI, bool NORM>
+// int8 (or, W4, int4) weights, 1-4 tokens: the row kernel with a larger
+// activation stage.
+template <int DT, int EPI, bool NORM, bool W4>
 static hipError_t gemv_row_w8_launch(const ProjArgs& a, hipStream_t s) {
   constexpr int NWV = NORM ? 4 : 16;
   // Features per workgroup: NWV rows (two per wave for one token), halved for
@@ -564,19 +604,19 @@ static hipError_t gemv_row_w8_launch(const ProjArgs& a, hipStream_t s) {
     LL_LAUNCH(k, dim3(grid), dim3(NWV * 64), sh, s, a);
     return hipGetLastError();
   };
-  if (a.M == 1) return go(gemv_row1_kernel<DT, EPI, NORM, 1, NWV, true>);
-  return go(gemv_row1_kernel<DT, EPI, NORM, 4, NWV, true>);
+  if (a.M == 1) return go(gemv_row1_kernel<DT, EPI, NORM, 1, NWV, true, W4>);
+  return go(gemv_row1_kernel<DT, EPI, NORM, 4, NWV, true, W4>);
 }
 
-template <int DT>
+template <int DT, bool W4>
 static hipError_t gemv_w8_dt(int epi, const ProjArgs& a, hipStream_t s) {
   const bool norm = a.gamma != nullptr;
   switch (epi) {
-    case EPI_QKV: return norm ? gemv_row_w8_launch<DT, EPI_QKV, true>(a, s)
-                              : gemv_row_w8_launch<DT, EPI_QKV, false>(a, s);
-    case EPI_RESID: return gemv_row_w8_launch<DT, EPI_RESID, false>(a, s);
-    case EPI_SWIGLU: return norm ? gemv_row_w8_launch<DT, EPI_SWIGLU, true>(a, s)
-                                 : gemv_row_w8_launch<DT, EPI_SWIGLU, false>(a, s);
+    case EPI_QKV: return norm ? gemv_row_w8_launch<DT, EPI_QKV, true, W4>(a, s)
+                              : gemv_row_w8_launch<DT, EPI_QKV, false, W4>(a, s);
+    case EPI_RESID: return gemv_row_w8_launch<DT, EPI_RESID, false, W4>(a, s);
+    case EPI_SWIGLU: return norm ? gemv_row_w8_launch<DT, EPI_SWIGLU, true, W4>(a, s)
+                                 : gemv_row_w8_launch<DT, EPI_SWIGLU, false, W4>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -587,13 +627,23 @@ bool gemv_w8_fits(int dt, int M, int K) {
 
 hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s) {
   if (!a.wscale[0]) return hipErrorInvalidValue;
+  if (a.wbits == 4) {
+    // int4: the row kernel only (1-4 tokens, K a multiple of 32).
+    if (!gemv_w8_fits(dt, a.M, a.K) || a.K % 32) return hipErrorInvalidValue;
+    switch (dt) {
+      case DT_F32: return gemv_w8_dt<DT_F32, true>(epi, a, s);
+      case DT_BF16: return gemv_w8_dt<DT_BF16, true>(epi, a, s);
+      case DT_F16: return gemv_w8_dt<DT_F16, true>(epi, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   // More tokens (or a stage that does not fit) go through the LDS-streaming
   // kernel, which reads every weight once for up to 32 tokens.
   if (!gemv_w8_fits(dt, a.M, a.K)) return launch_gemv_dma_w8(dt, epi, a, s);
   switch (dt) {
-    case DT_F32: return gemv_w8_dt<DT_F32>(epi, a, s);
-    case DT_BF16: return gemv_w8_dt<DT_BF16>(epi, a, s);
-    case DT_F16: return gemv_w8_dt<DT_F16>(epi, a, s);
+    case DT_F32: return gemv_w8_dt<DT_F32, false>(epi, a, s);
+    case DT_BF16: return gemv_w8_dt<DT_BF16, false>(epi, a, s);
+    case DT_F16: return gemv_w8_dt<DT_F16, false>(epi, a, s);
   }
   return hipErrorInvalidValue;
 }

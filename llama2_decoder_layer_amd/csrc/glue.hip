@@ -133,6 +133,44 @@ __global__ __launch_bounds__(256) void quantize_w8_kernel(const void* w, int8_t*
   }
 }
 
+// Weight-only int4 by rows: scale = max|w| / 7, code = rint(w / scale)
+// clipped to [-7, 7] (a zero row: scale 0, codes 0), packed two to a byte:
+// weight 2j in the low nibble of byte j, weight 2j + 1 in the high one.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_w4_kernel(const void* w, uint8_t* q, float* scale,
+                                                          int cols) {
+  typedef typename Elt<DT>::T T;
+  __shared__ float red[4];
+  const T* r = reinterpret_cast<const T*>(w) + (size_t)blockIdx.x * cols;
+  uint8_t* qr = q + (size_t)blockIdx.x * (cols / 2);
+  float m = 0.f;
+  for (int c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(Elt<DT>::to_f32(r[c])));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(m, 7.0f);
+  if (threadIdx.x == 0) scale[blockIdx.x] = s;
+  auto code = [&](int c) -> uint32_t {
+    float v = 0.f;
+    if (s > 0.f) v = fminf(7.f, fmaxf(-7.f, rintf(__fdiv_rn(Elt<DT>::to_f32(r[c]), s))));
+    return (uint32_t)(int)v & 15u;
+  };
+  for (int j = threadIdx.x; j < cols / 2; j += 256)
+    qr[j] = (uint8_t)(code(2 * j) | (code(2 * j + 1) << 4));
+}
+
+hipError_t launch_quantize_w4(int dt, const void* w, uint8_t* q, float* scale, int rows, int cols,
+                              hipStream_t s) {
+  if (dt == DT_F32)
+    LL_LAUNCH(quantize_w4_kernel<DT_F32>, dim3(rows), dim3(256), 0, s, w, q, scale, cols);
+  else if (dt == DT_BF16)
+    LL_LAUNCH(quantize_w4_kernel<DT_BF16>, dim3(rows), dim3(256), 0, s, w, q, scale, cols);
+  else
+    LL_LAUNCH(quantize_w4_kernel<DT_F16>, dim3(rows), dim3(256), 0, s, w, q, scale, cols);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_w8(int dt, const void* w, int8_t* q, float* scale, int rows, int cols,
                               hipStream_t s) {
   if (dt == DT_F32)

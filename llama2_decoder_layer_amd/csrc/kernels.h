@@ -65,7 +65,8 @@ struct ProjArgs {
   const float* rcos;
   const float* rsin;
   float* part;        // float32 K-split partials of the streaming projection (workspace)
-  const float* wscale[3];  // int8 weights: float32 scale per row of each segment
+  const float* wscale[3];  // int8 / int4 weights: float32 scale per row of each segment
+  int wbits;               // quantised weights: 8 (int8 codes) or 4 (packed int4 codes)
   KvPages pages;           // paged caches (pages.table == nullptr: contiguous)
 };
 
@@ -79,6 +80,8 @@ bool gemv_fits_lds(int dt, int M, int K);
 constexpr int GEMV_W8_LDS_BYTES = 128 * 1024;
 bool gemv_w8_fits(int dt, int M, int K);
 hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
+// a.wbits == 4: packed int4 codes (weight 2j in the low nibble of byte j,
+// rows of K/2 bytes), K % 32 == 0, and only what gemv_w8_fits admits.
 // Weight-only int8 through the LDS-streaming kernel (16-bit activations, M <= 32,
 // K % 64 == 0, no fused norm; partials as gemv_dma_partial_floats).
 hipError_t launch_gemv_dma_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
@@ -89,6 +92,8 @@ hipError_t launch_kv_pages_write(const void* k_src, const void* v_src, int s_max
                                  int batch, int nkv, int hd, int kv_dt, hipStream_t s);
 // Per-row symmetric int8 codes and float32 scales of a [rows, cols] matrix.
 hipError_t launch_quantize_w8(int dt, const void* w, int8_t* q, float* scale, int rows, int cols,
+                              hipStream_t s);
+hipError_t launch_quantize_w4(int dt, const void* w, uint8_t* q, float* scale, int rows, int cols,
                               hipStream_t s);
 // Prefill projection (M tokens): MFMA tiles with fused epilogues.  When the
 // last round of 256 x 256 tiles would leave CUs idle, its tiles are split

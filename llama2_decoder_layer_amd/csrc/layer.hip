@@ -193,13 +193,15 @@ static ProjArgs base_args(const ll_config* c) {
 }
 
 // Token-skinny plan for tokens [tok0, tok0 + m) of B*T.
-// With w8 set (and w unused) the projections take int8 weights and per-row
-// scales through the int8 row kernel; m is then at most 4.
+// With w8 set (and w unused) the projections take quantised weights and
+// per-row scales: int8 codes (wbits 8) or packed int4 codes (wbits 4, the
+// fields then point to the packed rows; m at most 4).
 // With pages.table set, kc and vc are the pools of a paged cache.
 static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_w8* w8,
                       const void* x, void* y, void* kc, void* vc, const int32_t* ctx_len,
                       int start_pos, int T, int max_ctx, int s_max, int64_t tok0, int m,
-                      uint8_t* ws, const Layout& L, hipStream_t s, const KvPages& pages = {}) {
+                      uint8_t* ws, const Layout& L, hipStream_t s, const KvPages& pages = {},
+                      int wbits = 8) {
   const int dt = c->act_dtype;
   const size_t act = esize(dt);
   const int H = c->hidden, I = c->intermediate;
@@ -217,7 +219,10 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
   const void* attn_norm = w8 ? w8->attn_norm : w->attn_norm;
   const void* ffn_norm = w8 ? w8->ffn_norm : w->ffn_norm;
   auto proj = [&](int epi, const ProjArgs& pa) {
-    return w8 ? launch_gemv_w8(dt, epi, pa, s) : launch_gemv(dt, epi, pa, s);
+    if (!w8) return launch_gemv(dt, epi, pa, s);
+    ProjArgs q = pa;
+    q.wbits = wbits;
+    return launch_gemv_w8(dt, epi, q, s);
   };
 
   float* part = (float*)(ws + L.part);
@@ -637,6 +642,70 @@ int llama_layer_decode_w8(const ll_config* cfg, const ll_weights_w8* w, const vo
     const int m = std::min(g, batch - b0);
     rc = run_skinny(cfg, nullptr, w, x, y, k_cache, v_cache, ctx_len, 0, 1, max_ctx, s_max, b0, m,
                     (uint8_t*)ws, L, s);
+    if (rc) return rc;
+  }
+  return LL_OK;
+}
+
+int llama_quantize_w4(const void* w, uint8_t* q, float* scale, int32_t rows, int32_t cols,
+                      int32_t dtype, void* stream) {
+  int rc = check_ptrs({w, q});
+  if (rc) return rc;
+  if ((rc = check_ptrs4({scale}))) return rc;
+  if (rows <= 0 || cols <= 0 || cols % 32 || dtype < LL_F32 || dtype > LL_F16) return LL_EINVAL;
+  (void)hipGetLastError();
+  if (launch_quantize_w4(dtype, w, q, scale, rows, cols, (hipStream_t)stream) != hipSuccess)
+    return LL_EHIP;
+  return LL_OK;
+}
+
+int llama_layer_decode_w4(const ll_config* cfg, const ll_weights_w4* w, const void* x, void* y,
+                          void* k_cache, void* v_cache, const int32_t* ctx_len, int32_t batch,
+                          int32_t max_ctx, int32_t s_max, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w) return LL_ENULL;
+  if ((rc = check_ptrs({w->attn_norm, w->ffn_norm, w->w_q, w->w_k, w->w_v, w->w_o, w->w_gate,
+                        w->w_up, w->w_down, w->rope_cos, w->rope_sin})))
+    return rc;
+  if ((rc = check_ptrs4({w->s_q, w->s_k, w->s_v, w->s_o, w->s_gate, w->s_up, w->s_down})))
+    return rc;
+  if ((rc = check_ptrs({x, y, k_cache, v_cache}))) return rc;
+  if ((rc = check_ptrs4({ctx_len}))) return rc;
+  if (batch <= 0 || max_ctx < 0 || s_max <= 0) return LL_EINVAL;
+  if (cfg->hidden % 32 || cfg->intermediate % 32 || (cfg->n_heads * cfg->head_dim) % 32)
+    return LL_EINVAL;
+  if ((int64_t)max_ctx + 1 > s_max || (int64_t)max_ctx + 1 > cfg->max_pos) return LL_ECACHE_FULL;
+  // Groups of at most 4 sequences through the row kernel.
+  const int kmax = std::max(std::max(cfg->hidden, cfg->intermediate),
+                            cfg->n_heads * cfg->head_dim);
+  int g = 4;
+  while (g > 0 && !gemv_w8_fits(cfg->act_dtype, g, kmax)) --g;
+  if (g < 1) return LL_EUNSUPPORTED;
+  const size_t act = esize(cfg->act_dtype);
+  if (overlap(x, (size_t)batch * cfg->hidden * act, y, (size_t)batch * cfg->hidden * act))
+    return LL_EINVAL;
+  const Layout L = layout(cfg, batch, s_max, false);
+  if (!ws) return LL_EWORKSPACE;
+  if (!aligned16(ws)) return LL_EALIGN;
+  if (ws_bytes < L.total) return LL_EWORKSPACE;
+  // Same field layout as the int8 weights; the kernels read packed int4 rows.
+  ll_weights_w8 w8;
+  w8.attn_norm = w->attn_norm; w8.ffn_norm = w->ffn_norm;
+  w8.w_q = (const int8_t*)w->w_q; w8.w_k = (const int8_t*)w->w_k;
+  w8.w_v = (const int8_t*)w->w_v; w8.w_o = (const int8_t*)w->w_o;
+  w8.w_gate = (const int8_t*)w->w_gate; w8.w_up = (const int8_t*)w->w_up;
+  w8.w_down = (const int8_t*)w->w_down;
+  w8.s_q = w->s_q; w8.s_k = w->s_k; w8.s_v = w->s_v; w8.s_o = w->s_o;
+  w8.s_gate = w->s_gate; w8.s_up = w->s_up; w8.s_down = w->s_down;
+  w8.rope_cos = w->rope_cos; w8.rope_sin = w->rope_sin;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  for (int b0 = 0; b0 < batch; b0 += g) {
+    const int m = std::min(g, batch - b0);
+    rc = run_skinny(cfg, nullptr, &w8, x, y, k_cache, v_cache, ctx_len, 0, 1, max_ctx, s_max, b0,
+                    m, (uint8_t*)ws, L, s, KvPages{}, 4);
     if (rc) return rc;
   }
   return LL_OK;

@@ -149,6 +149,11 @@ WORKLOADS = {
     "decode_7b_b1_ctx4096_w8": Workload("decode_7b_b1_ctx4096_w8", 7, L7B, "bf16", "bf16",
                                         "decode", batch=1, ctx=4096, s_max=4097,
                                         extra={"w8": True}),
+    # The same 7B decode with weight-only INT4 projections (same weights and
+    # inputs as the INT8 one: seed index 7).
+    "decode_7b_b1_ctx4096_w4": Workload("decode_7b_b1_ctx4096_w4", 7, L7B, "bf16", "bf16",
+                                        "decode", batch=1, ctx=4096, s_max=4097,
+                                        extra={"w4": True}),
     # Sampling after the LM head: 32 rows of a 32000-token vocabulary with the
     # pages' dialogue settings and 256 previous ids per row.
     "sample_b32_v32000": Workload("sample_b32_v32000", 6, L70B, "f32", "f32", "sample",

@@ -201,6 +201,12 @@ def test_glue_validation():
     assert Q(FAKE, FAKE, FAKE, 4, 40, 1, None) == -1      # cols % 16
     assert Q(FAKE, FAKE, FAKE, 0, 32, 1, None) == -1
     assert Q(FAKE, FAKE, FAKE, 4, 32, 9, None) == -1      # dtype
+    Q4 = L.llama_quantize_w4
+    assert Q4(None, FAKE, FAKE, 4, 64, 1, None) == -2
+    assert Q4(FAKE, FAKE, FAKE + 2, 4, 64, 1, None) == -3
+    assert Q4(FAKE, FAKE, FAKE, 4, 48, 1, None) == -1     # cols % 32
+    assert Q4(FAKE, FAKE, FAKE, -1, 64, 1, None) == -1
+    assert Q4(FAKE, FAKE, FAKE, 4, 64, 3, None) == -1     # dtype
     assert L.llama_embed(FAKE, FAKE, FAKE, 0, 256, 512, 1, None) == -1
     assert L.llama_embed(FAKE, FAKE + 2, FAKE, 1, 256, 512, 1, None) == -3
     assert L.llama_embed(FAKE, FAKE, FAKE, 1, 256, 512, 7, None) == -1
@@ -272,4 +278,25 @@ def test_w8_decode_validation():
     assert rc(s_up=FAKE + 2) == -3
     assert rc(c=cfg(intermediate=680)) == -1             # not a multiple of 16
     assert B.lib().llama_layer_decode_w8(ctypes.byref(c), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1,
+                                         32, FAKE, 1, None) == -2
+
+
+def test_w4_decode_validation():
+    c = cfg(intermediate=704)
+    names = [n for n, _ in B.ll_weights_w4._fields_]
+    ptrs = {n: FAKE + 256 * i for i, n in enumerate(names)}
+
+    def rc(c=c, **kw):
+        p = dict(ptrs)
+        p.update(kw)
+        w = B.ll_weights_w4(*[p[n] for n in names])
+        return B.lib().llama_layer_decode_w4(ctypes.byref(c), ctypes.byref(w), FAKE + 0x100000,
+                                             FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                             FAKE + 0x600000, 2, 10, 32, FAKE + 0x500000, 1, None)
+    assert rc() == -5                                    # workspace too small
+    assert rc(w_q=None) == -2
+    assert rc(s_o=None) == -2
+    assert rc(s_down=FAKE + 1) == -3
+    assert rc(c=cfg(intermediate=688)) == -1             # not a multiple of 32
+    assert B.lib().llama_layer_decode_w4(ctypes.byref(c), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1,
                                          32, FAKE, 1, None) == -2
