@@ -20,7 +20,7 @@
  * object written at the current position).
  *
  * Around the layer: the same layer over a paged KV cache (decode and chunked
- * prefill), with weight-only INT8 projections (decode), RoPE tables (also
+ * prefill), with weight-only INT8 or INT4 projections (decode), RoPE tables (also
  * NTK-scaled for longer contexts), embedding lookup, the LM head with a
  * greedy pick, and a fused sampler (penalty, temperature, top-k, top-p).
  *
