@@ -488,38 +488,38 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        continue;
-      }
-      float wf[RPW][EW];
+      } else {
+        float wf[RPW][EW];
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        if constexpr (WQ) {
+        for (int r = 0; r < RPW; ++r) {
+          if constexpr (WQ) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-              wf[r][4 * i + b] = (float)(int8_t)(wv[r][u][i] >> (8 * b));
-        } else {
-          unpack16<DT>(wv[r][u], wf[r]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-#pragma unroll
-          for (int h = 0; h < EW / E; ++h) {
-            float xf[E];
-            unpack16<DT>(ld16(xs + (size_t)m * K + k + h * E), xf);
-#pragma unroll
-            for (int r = 0; r < RPW; ++r)
-#pragma unroll
-              for (int e = 0; e < E; ++e) acc[r][m] += wf[r][h * E + e] * xf[e];
+              for (int b = 0; b < 4; ++b)
+                wf[r][4 * i + b] = (float)(int8_t)(wv[r][u][i] >> (8 * b));
+          } else {
+            unpack16<DT>(wv[r][u], wf[r]);
           }
         }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < M) {
+#pragma unroll
+            for (int h = 0; h < EW / E; ++h) {
+              float xf[E];
+              unpack16<DT>(ld16(xs + (size_t)m * K + k + h * E), xf);
+#pragma unroll
+              for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[r][m] += wf[r][h * E + e] * xf[e];
+            }
+          }
+        }
+        // int8: keep each chunk's conversions and activation reads next to
+        // their use; hoisted across the batch they exhaust the registers.
+        if constexpr (WQ) __builtin_amdgcn_sched_barrier(0);
       }
-      // int8: keep each chunk's conversions and activation reads next to
-      // their use; hoisted across the batch they exhaust the registers.
-      if constexpr (WQ) __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
