@@ -466,6 +466,21 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
         // 32-bit word of each row.
 #pragma unroll
         for (int h = 0; h < EW / E; ++h) {
+          if constexpr (MT == 1) {
+            // One token: each code is used once, so convert it at its FMA
+            // (fewer live registers, more waves per SIMD).
+            float xf[E];
+            unpack16<DT>(ld16(xs + k + h * E), xf);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                const int idx = h * E + e;
+                const uint32_t word = wv[r][u][idx >> 3];
+                acc[r][0] += (float)((int32_t)(word << (28 - 4 * (idx & 7))) >> 28) * xf[e];
+              }
+            continue;
+          }
           float wf4[RPW][E];
 #pragma unroll
           for (int r = 0; r < RPW; ++r)
