@@ -282,8 +282,9 @@ typedef struct ll_weights_w4 {
  * (llama_layer_workspace_size with tokens = 1), caches and results, the
  * projections reading half a byte per weight.  Sequences go through in groups
  * of up to 4 (fewer when 4 rows of the longest reduction would not fit the
- * 128 KB activation stage), each group reading every weight once.  hidden,
- * intermediate and n_heads * head_dim must be multiples of 32.
+ * 128 KB activation stage), each group reading every weight once, so beyond
+ * 8 sequences llama_layer_decode_w8 (up to 32 per weight pass) reads fewer
+ * bytes.  hidden, intermediate and n_heads * head_dim must be multiples of 32.
  * Errors: as llama_layer_decode; LL_EUNSUPPORTED when a single row of the
  * longest reduction does not fit the stage.
  */
