@@ -343,7 +343,7 @@ int llama_head_argmax(const void* final_norm, const void* w_lm, const void* h,
 /*
  * Token sampling after the LM head ("Llama2架构与推理全解析" §2.5 for the
  * steps, §3.3 for typical settings -- temperature 0.7, top-p 0.9, top-k 50,
- * repetition penalty 1.1; "Llama2架构全景解析" §3 draws from
+ * repetition penalty 1.1; "Llama2架构全景解析" §2.2, step 3, draws from
  * softmax(logits / T)).  For each row r:
  *   1. every distinct id of history[r] lowers its logit: divided by
  *      `penalty` if positive, multiplied by it otherwise (penalty 1: off);

@@ -89,6 +89,32 @@ __device__ __forceinline__ void gemv_finish(const ProjArgs& a, f32x4 (&acc)[NA][
   }
 }
 
+// Fused RMSNorm, f16: the staging pass stored the raw rows and the sums of
+// squares; this second pass over LDS turns each into x * rstd * gain (the
+// separate norm pass's arithmetic).  Staging x * gain and applying rstd after
+// the dot products, as the 32-bit and bf16 paths do, could overflow f16's
+// range (65504) where the normalised value cannot: |x * rstd| <= sqrt(K).
+// Each thread rewrites the chunks it staged, so only the rstd needs a barrier.
+template <int DT>
+__device__ __forceinline__ void stage_prescaled(typename Elt<DT>::T* xs,
+                                                const typename Elt<DT>::T* gg,
+                                                const float* rstd_s, int M, int K, int tid,
+                                                int nthreads) {
+  constexpr int E = Elt<DT>::PER16;
+  const int KC = K / E;
+  for (int m = 0; m < M; ++m) {
+    const float r = rstd_s[m];
+    for (int c = tid; c < KC; c += nthreads) {
+      float xf[E], gf[E];
+      unpack16<DT>(ld16(xs + (size_t)m * K + c * E), xf);
+      unpack16<DT>(ld16(gg + c * E), gf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) xf[e] = xf[e] * r * gf[e];
+      st16(xs + (size_t)m * K + c * E, pack16<DT>(xf));
+    }
+  }
+}
+
 // Weight row pointers of this lane (rows past N read row 0; dropped later).
 template <int DT, int EPI, int NA>
 __device__ __forceinline__ void gemv_rows(const ProjArgs& a, int row0,
@@ -146,7 +172,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_lds_kernel(ProjArgs a) {
     if (kb0 + 1 < kb1) load_w(ic<1>{}, kb0 + 1);
   }
 
-  // Stage activations (times the gain when the norm is fused).
+  // Stage activations (times the gain when the norm is fused; f16 stages the
+  // normalised rows instead, see stage_prescaled).
+  constexpr bool PRE = NORM && DT == DT_F16;
   const int KC = K / E;
   const T* xg = reinterpret_cast<const T*>(a.x);
   const T* gg = reinterpret_cast<const T*>(a.gamma);
@@ -157,13 +185,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_lds_kernel(ProjArgs a) {
       if constexpr (NORM) {
         float xf[E], gf[E];
         unpack16<DT>(xv, xf);
-        unpack16<DT>(ld16(gg + c * E), gf);
+        if constexpr (!PRE) unpack16<DT>(ld16(gg + c * E), gf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           ss += xf[e] * xf[e];
-          xf[e] *= gf[e];
+          if constexpr (!PRE) xf[e] *= gf[e];
         }
-        xv = pack16<DT>(xf);
+        if constexpr (!PRE) xv = pack16<DT>(xf);
       }
       st16(xs + (size_t)m * K + c * E, xv);
     }
@@ -180,6 +208,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_lds_kernel(ProjArgs a) {
       __syncthreads();
     }
   }
+  if constexpr (PRE) stage_prescaled<DT>(xs, gg, rstd_s, M, K, tid, NW * 64);
   __syncthreads();
 
   f32x4 acc[NA][1];
@@ -207,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_lds_kernel(ProjArgs a) {
       if (kb + 2 < kb1) step(ic<2 % NS>{}, kb + 2);
     }
   }
-  gemv_finish<DT, EPI, NA, 1, NW>(a, acc, NORM ? rstd_s : nullptr, row0);
+  gemv_finish<DT, EPI, NA, 1, NW>(a, acc, (NORM && !PRE) ? rstd_s : nullptr, row0);
 }
 
 template <int DT, int EPI, int CT, int NW, int PF>
@@ -415,6 +444,7 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
   // Weight loads start before the activations are staged.
   load_batch(0);
 
+  constexpr bool PRE = NORM && DT == DT_F16;  // see stage_prescaled
   const int KC = K / E;
   const T* xg = reinterpret_cast<const T*>(a.x);
   const T* gg = reinterpret_cast<const T*>(a.gamma);
@@ -425,13 +455,13 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
       if constexpr (NORM) {
         float xf[E], gf[E];
         unpack16<DT>(xv, xf);
-        unpack16<DT>(ld16(gg + c * E), gf);
+        if constexpr (!PRE) unpack16<DT>(ld16(gg + c * E), gf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           ss += xf[e] * xf[e];
-          xf[e] *= gf[e];
+          if constexpr (!PRE) xf[e] *= gf[e];
         }
-        xv = pack16<DT>(xf);
+        if constexpr (!PRE) xv = pack16<DT>(xf);
       }
       st16(xs + (size_t)m * K + c * E, xv);
     }
@@ -448,6 +478,7 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
       __syncthreads();
     }
   }
+  if constexpr (PRE) stage_prescaled<DT>(xs, gg, rstd_s, M, K, tid, NWV * 64);
   __syncthreads();
 
   float acc[RPW][MT];
@@ -557,7 +588,7 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
     const int m = tid / G4, g = tid - m * G4;
     const int f = f0 + 4 * g;
     if (f >= a.N) return;
-    const float scale = NORM ? rstd_s[m] : 1.f;
+    const float scale = (NORM && !PRE) ? rstd_s[m] : 1.f;
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = res_s[4 * g + i][m] * scale;
@@ -567,7 +598,7 @@ __global__ __launch_bounds__(NWV * 64) void gemv_row1_kernel(ProjArgs a) {
     const int m = tid / FW, i = tid - m * FW;
     const int f = f0 + i;
     if (f >= a.N) return;
-    const float scale = NORM ? rstd_s[m] : 1.f;
+    const float scale = (NORM && !PRE) ? rstd_s[m] : 1.f;
     const float v = res_s[i][m] * scale;
     if constexpr (EPI == EPI_LOGITS) {
       reinterpret_cast<float*>(a.y)[(size_t)m * a.N + f] = v;

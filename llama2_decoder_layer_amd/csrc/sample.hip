@@ -1,6 +1,6 @@
 // Token sampling after the LM head: repetition penalty, temperature, top-k,
 // softmax, top-p and the draw ("Llama2架构与推理全解析" §2.5 names the steps,
-// §3.3 gives typical settings; "Llama2架构全景解析" §3 draws from
+// §3.3 gives typical settings; "Llama2架构全景解析" §2.2, step 3, draws from
 // softmax(logits / T)).
 //
 // One 1024-thread workgroup per row.  Each thread keeps EPT = 32 logits of the

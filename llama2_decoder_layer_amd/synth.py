@@ -9,7 +9,9 @@ Storage forms: float32 arrays for ``f32``; uint16 bit patterns for ``bf16`` and
 ``f16`` (round-to-nearest-even from float32).
 
 Recipes (the workloads the pages describe, made synthetic):
-  * weights ~ N(0, 0.02) drawn in float32 then rounded; RMSNorm gains = 1;
+  * weights ~ N(0, 0.02) drawn in float32 then rounded; RMSNorm gains = 1 in
+    the benchmark workloads, and 1 + 0.3 N(0, 1) (rounded the same way) where
+    a parity case asks for learned gains;
   * prefill / decode hidden states ~ N(0, 1);
   * KV caches of decode workloads pre-filled with N(0, 1) values, read as keys
     that are already rotated;
@@ -174,6 +176,7 @@ WORKLOADS = {
 # pool and the values do not depend on the number of threads.
 
 WEIGHT_STD = 0.02
+GAIN_STD = 0.3             # learned gains: 1 + GAIN_STD * N(0, 1)
 LAYER_TENSORS = ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")
 CHUNK = 1 << 22
 STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16}
@@ -212,15 +215,30 @@ def normal(ss: np.random.SeedSequence, shape, std: float = 1.0, dtype: str = "f3
     return out
 
 
-def draw_layer(ss: np.random.SeedSequence, s: Shape, dtype: str) -> dict:
-    """One layer's weights in storage form; gains are ones."""
+def draw_gain(ss: np.random.SeedSequence, hidden: int, dtype: str) -> np.ndarray:
+    """A learned RMSNorm gain, 1 + GAIN_STD * N(0, 1), drawn in float32 and
+    rounded to `dtype` storage."""
+    g = np.random.Generator(np.random.PCG64(ss)).standard_normal(hidden, dtype=np.float32)
+    return to_storage(np.float32(1.0) + np.float32(GAIN_STD) * g, dtype)
+
+
+def draw_layer(ss: np.random.SeedSequence, s: Shape, dtype: str,
+               learned_gains: bool = False) -> dict:
+    """One layer's weights in storage form.  Gains are ones, or with
+    learned_gains two independent draws of draw_gain (the projection weights
+    are the same either way: the gains take the next two children)."""
     shapes = layer_tensor_shapes(s)
     kids = ss.spawn(len(LAYER_TENSORS))
     out = {name: normal(kid, shapes[name], WEIGHT_STD, dtype)
            for name, kid in zip(LAYER_TENSORS, kids)}
-    ones = np.ones(s.hidden, dtype=np.float32)
-    out["attn_norm"] = to_storage(ones, dtype)
-    out["ffn_norm"] = to_storage(ones, dtype)
+    if learned_gains:
+        k_attn, k_ffn = ss.spawn(2)
+        out["attn_norm"] = draw_gain(k_attn, s.hidden, dtype)
+        out["ffn_norm"] = draw_gain(k_ffn, s.hidden, dtype)
+    else:
+        ones = np.ones(s.hidden, dtype=np.float32)
+        out["attn_norm"] = to_storage(ones, dtype)
+        out["ffn_norm"] = to_storage(ones, dtype)
     return out
 
 
@@ -238,14 +256,19 @@ def draw_prompt(w: Workload) -> np.ndarray:
     return rng.integers(0, w.vocab, size=w.prompt, dtype=np.int64).astype(np.int32)
 
 
-def draw_stack(w: Workload) -> dict:
-    """Stack: layers, embedding table, final gain, LM head and the prompt."""
+def draw_stack(w: Workload, learned_gains: bool = False) -> dict:
+    """Stack: layers, embedding table, final gain, LM head and the prompt.
+    learned_gains draws every RMSNorm gain (the final one included) with
+    draw_gain instead of ones; the other tensors are unchanged."""
     ss = weights_seed(w.index)
     kids = ss.spawn(w.n_layers + 2)
-    layers = [draw_layer(kids[i], w.shape, w.act_dtype) for i in range(w.n_layers)]
+    layers = [draw_layer(kids[i], w.shape, w.act_dtype, learned_gains) for i in range(w.n_layers)]
     embed = normal(kids[w.n_layers], (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype)
     w_lm = normal(kids[w.n_layers + 1], (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype)
-    final_norm = to_storage(np.ones(w.shape.hidden, np.float32), w.act_dtype)
+    if learned_gains:
+        final_norm = draw_gain(ss.spawn(1)[0], w.shape.hidden, w.act_dtype)
+    else:
+        final_norm = to_storage(np.ones(w.shape.hidden, np.float32), w.act_dtype)
     return dict(layers=layers, embed=embed, w_lm=w_lm, final_norm=final_norm,
                 prompt=draw_prompt(w))
 
@@ -270,26 +293,44 @@ def device_normal(seed: int, tensor_id: int, shape, std: float, dtype: str, devi
     return t.to({"bf16": torch.bfloat16, "f16": torch.float16}[dtype])
 
 
-def draw_stack_device(w: Workload, device="cuda") -> dict:
-    """The stack drawn on the device: layers (dicts of tensors, gains are ones),
-    embedding table, final gain and LM head; the prompt stays a host array."""
+def device_gain(seed: int, tensor_id: int, hidden: int, dtype: str, device="cuda"):
+    """A learned gain drawn on the device: 1 + GAIN_STD * N(0, 1) in float32
+    from the (seed, tensor id) stream, rounded to the storage format."""
+    import torch
+    g = device_normal(seed, tensor_id, (hidden,), GAIN_STD, "f32", device) + 1.0
+    if dtype == "f32":
+        return g
+    return g.to({"bf16": torch.bfloat16, "f16": torch.float16}[dtype])
+
+
+def draw_stack_device(w: Workload, device="cuda", learned_gains: bool = False) -> dict:
+    """The stack drawn on the device: layers (dicts of tensors), embedding
+    table, final gain and LM head; the prompt stays a host array.  Gains are
+    ones, or with learned_gains device_gain draws (tensor ids 7 and 8 of each
+    layer, the final one after the LM head)."""
     import torch
     seed = 1000 + w.index
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act_dtype]
     shapes = layer_tensor_shapes(w.shape)
+    H = w.shape.hidden
+
+    def gain(tid):
+        if learned_gains:
+            return device_gain(seed, tid, H, w.act_dtype, device)
+        return torch.ones(H, dtype=tdt, device=device)
+
     layers = []
     for l in range(w.n_layers):
         d = {name: device_normal(seed, l * DEVICE_TENSOR_IDS + i, shapes[name], WEIGHT_STD,
                                  w.act_dtype, device)
              for i, name in enumerate(LAYER_TENSORS)}
-        d["attn_norm"] = torch.ones(w.shape.hidden, dtype=tdt, device=device)
-        d["ffn_norm"] = torch.ones(w.shape.hidden, dtype=tdt, device=device)
+        d["attn_norm"] = gain(l * DEVICE_TENSOR_IDS + len(LAYER_TENSORS))
+        d["ffn_norm"] = gain(l * DEVICE_TENSOR_IDS + len(LAYER_TENSORS) + 1)
         layers.append(d)
     base = w.n_layers * DEVICE_TENSOR_IDS
-    embed = device_normal(seed, base, (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype, device)
-    w_lm = device_normal(seed, base + 1, (w.vocab, w.shape.hidden), WEIGHT_STD, w.act_dtype,
-                         device)
-    final_norm = torch.ones(w.shape.hidden, dtype=tdt, device=device)
+    embed = device_normal(seed, base, (w.vocab, H), WEIGHT_STD, w.act_dtype, device)
+    w_lm = device_normal(seed, base + 1, (w.vocab, H), WEIGHT_STD, w.act_dtype, device)
+    final_norm = gain(base + 2)
     return dict(layers=layers, embed=embed, w_lm=w_lm, final_norm=final_norm,
                 prompt=draw_prompt(w))
 

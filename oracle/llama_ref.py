@@ -39,7 +39,12 @@ Pins (tests/test_oracle_*.py, all CPU):
   layer_prefill   transformers' LlamaDecoderLayer in float64 (RoPE layouts
                   related by a fixed row permutation of W_q/W_k).
   layer_decode    prefill(T) then k decodes equals prefill(T + k).
-  greedy/stack    argmax lowest-index tie break; cached generation equals
+  embed           one-hot rows times the table.
+  lm_head         a hand-worked two-row example (final gain, eps inside the
+                  root, untied W_lm), torch rms_norm followed by a linear layer.
+  greedy/stack    argmax lowest-index tie break; with no layers, generation is
+                  the head alone on the prompt's last token and then on each
+                  previous id (torch); cached generation equals
                   full-recompute generation.
   quantize_w8     the round-to-nearest bound |w - q s| <= s/2, the largest
                   magnitude on +-127, sign symmetry, exact re-quantisation of
@@ -361,7 +366,7 @@ def dequantize_w4(codes, scales) -> np.ndarray:
 def sampling_distribution(logits, history, temperature: float, top_k: int, top_p: float,
                           penalty: float):
     """The distribution one token is drawn from ("Llama2架构与推理全解析" §2.5;
-    "Llama2架构全景解析" §3 draws from softmax(logits / T)).
+    "Llama2架构全景解析" §2.2, step 3, draws from softmax(logits / T)).
 
     Steps in the pages' order: the repetition penalty lowers every token that
     already occurred (a positive logit is divided by `penalty`, a negative

@@ -95,8 +95,16 @@ class DeviceLayer:
         return y
 
 
-def random_layer(shape: S.Shape, act: str, seed: int) -> dict:
-    return S.draw_layer(np.random.SeedSequence(seed), shape, act)
+def random_layer(shape: S.Shape, act: str, seed: int, learned_gains: bool = True) -> dict:
+    """A parity case's layer: N(0, 0.02) weights and learned RMSNorm gains
+    (1 + 0.3 N(0, 1), a different draw for attn_norm and ffn_norm), so that a
+    kernel that ignored a gain or swapped the two would fail."""
+    return S.draw_layer(np.random.SeedSequence(seed), shape, act, learned_gains=learned_gains)
+
+
+def scale_stored(a, dtype, factor):
+    """Multiply stored values by a power of two (exact in every format)."""
+    return S.to_storage((S.to_f64(a, dtype) * factor).astype(np.float32), dtype)
 
 
 # Half an ulp, relative to the value, of the format the layer stores out and

@@ -438,6 +438,77 @@ def check_greedy_ties():
     assert list(R.greedy(np.array([[0.0, 5.0, 5.0], [7.0, 7.0, 1.0]]))) == [1, 0]
 
 
+def check_embed_one_hot():
+    """Embedding lookup is the one-hot row vector of each id times the table."""
+    r = _rng(23)
+    table = r.standard_normal((11, 6))
+    ids = np.array([0, 10, 3, 3, 7])
+    onehot = np.zeros((len(ids), 11))
+    onehot[np.arange(len(ids)), ids] = 1.0
+    assert np.array_equal(R.embed(table, ids), onehot @ table)
+
+
+def check_lm_head_worked_example():
+    """A hand-worked output head ("Llama2架构与推理全解析" §2.3: final RMSNorm,
+    then the untied LM head; "Llama2架构全景解析" §2.2 step 2).
+
+    hidden 2, eps 3.5, gain (2, -1).  Row (3, 4): mean square 12.5, so
+    sqrt(12.5 + 3.5) = 4 and the normalised row is (0.75, 1) * (2, -1) =
+    (1.5, -1).  Row (-3, 4): (-0.75, 1) * (2, -1) = (-1.5, -1).  With W_lm
+    rows (1, 0), (0, 1), (1, 1), (-2, 0.5) the logits are (1.5, -1, 0.5, -3.5)
+    and (-1.5, -1, -2.5, 2.5): greedy ids 0 and 3.
+    """
+    h = np.array([[3.0, 4.0], [-3.0, 4.0]])
+    gain = np.array([2.0, -1.0])
+    w_lm = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [-2.0, 0.5]])
+    lg = R.lm_head(h, gain, w_lm, 3.5)
+    want = np.array([[1.5, -1.0, 0.5, -3.5], [-1.5, -1.0, -2.5, 2.5]])
+    assert np.max(np.abs(lg - want)) < 1e-15, lg
+    assert list(R.greedy(lg)) == [0, 3]
+
+
+def check_lm_head_torch():
+    """lm_head equals torch's rms_norm followed by a linear layer, in float64,
+    with a learned final gain and a large eps (so its place shows)."""
+    r = _rng(24)
+    H, V = 48, 37
+    h = r.standard_normal((5, H)) * np.array([[0.05], [0.3], [1.0], [4.0], [0.01]])
+    gain = 1.0 + 0.3 * r.standard_normal(H)
+    w_lm = r.standard_normal((V, H))
+    for eps in (1e-5, 0.05):
+        want = F.linear(F.rms_norm(torch.from_numpy(h), (H,), torch.from_numpy(gain), eps),
+                        torch.from_numpy(w_lm)).numpy()
+        assert rel_err(R.lm_head(h, gain, w_lm, eps), want) < 1e-13
+
+
+def check_generate_head_leg():
+    """With no layers, greedy generation is the head alone: the first id comes
+    from the prompt's last token, each later one from the previous id, through
+    the final RMSNorm (learned gain) and W_lm, not the embedding table
+    ("Llama2架构与推理全解析" §2.3, §2.5).  Evaluated with torch."""
+    r = _rng(25)
+    H, V = 16, 29
+    emb = r.standard_normal((V, H))
+    w_lm = r.standard_normal((V, H))
+    gain = 1.0 + 0.3 * r.standard_normal(H)
+    eps = 0.05
+    cfg = rand_cfg(H, 2, 1, 8, 24, eps=eps)
+    prompt = np.array([3, 17, 8, 21])
+
+    def head(i):
+        x = torch.from_numpy(emb[i][None])
+        return F.linear(F.rms_norm(x, (H,), torch.from_numpy(gain), eps),
+                        torch.from_numpy(w_lm)).numpy()[0]
+
+    ids, logits = R.generate_greedy(cfg, [], emb, gain, w_lm, prompt, 5, 16)
+    prev = int(prompt[-1])
+    for step in range(6):
+        want = head(prev)
+        assert rel_err(logits[step], want) < 1e-13, step
+        assert ids[step] == int(np.argmax(want))
+        prev = int(ids[step])
+
+
 def check_stack_cached_equals_recompute():
     """Greedy generation with the KV cache picks the same ids as running the
     whole sequence again from scratch at every step."""
@@ -669,7 +740,8 @@ ALL_CHECKS = [
     check_attention_bruteforce, check_attention_invariants, check_attention_torch_sdpa,
     check_gqa_reductions, check_silu_closed_forms, check_swiglu_special_cases,
     check_layer_transformers, check_layer_cached_decode_equals_recompute,
-    check_layer_ragged_batch, check_greedy_ties, check_stack_cached_equals_recompute,
+    check_layer_ragged_batch, check_greedy_ties, check_embed_one_hot, check_lm_head_worked_example,
+    check_lm_head_torch, check_generate_head_leg, check_stack_cached_equals_recompute,
     check_sizes_golden, check_quantize_w8, check_quantize_w4, check_sampling_worked_example, check_sampling_inverse_cdf_counts,
     check_sampling_greedy_limits, check_sampling_transformers,
 ]

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from gpu_util import (TOL, DeviceLayer, check_errors, delta_error, from_dev, oracle_cfg,
-                      oracle_weights, random_layer, rel_err, to_dev)
+                      oracle_weights, random_layer, rel_err, scale_stored, to_dev)
 from llama2_decoder_layer_amd import binding as B
 from llama2_decoder_layer_amd import synth as S
 from oracle import llama_ref as R
@@ -57,7 +57,7 @@ def gather(pool, table, s_max):
 
 
 def run_paged_case(label, shape, act, kv, ctx_len, s_max, bs, seed, oracle=False, stored=None,
-                   inp=None):
+                   inp=None, x_scale=1.0):
     batch = len(ctx_len)
     say(f"[{label}] paged decode B={batch} ctx={[int(c) for c in ctx_len][:8]} s_max={s_max} "
         f"block={bs} {act}/{kv} {shape}")
@@ -66,6 +66,8 @@ def run_paged_case(label, shape, act, kv, ctx_len, s_max, bs, seed, oracle=False
     if inp is None:
         inp = S.draw_decode_inputs(np.random.SeedSequence(seed + 1), shape, batch, s_max, act, kv,
                                    ctx=0)
+    if x_scale != 1.0:
+        inp = dict(inp, x=scale_stored(inp["x"], act, x_scale))
     ctx = np.asarray(ctx_len, dtype=np.int32)
     dl = DeviceLayer(shape, stored, act, kv, max_pos=s_max)
     x = to_dev(inp["x"], act)
@@ -228,3 +230,11 @@ def test_kv_pages_write():
         want_v = np.zeros_like(v)
         want_v[:, :, 37:157] = v[:, :, 37:157]
         assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v), kv
+
+
+@pytest.mark.parametrize("ctx", [[77], [5, 200, 33]], ids=["1-token", "3-tokens"])
+def test_paged_branch_dominant(ctx):
+    """x scaled by 2^-8 so the branches dominate the output; paged == contiguous
+    bit for bit and the oracle's tolerance with no rounding allowance."""
+    run_paged_case("paged-small-x-" + str(len(ctx)), S.Shape(512, 8, 2, 128, 1376), "bf16", "f16",
+                   ctx, 256, 32, 190, oracle=True, x_scale=2.0 ** -8)

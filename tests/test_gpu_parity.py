@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from gpu_util import (TOL, DeviceLayer, check_errors, delta_error, from_dev, oracle_cfg,
-                      oracle_weights, random_layer, rel_err, to_dev)
+                      oracle_weights, random_layer, rel_err, scale_stored, to_dev)
 from llama2_decoder_layer_amd import synth as S
 from oracle import llama_ref as R
 
@@ -22,13 +22,8 @@ def say(msg):
     print(msg, flush=True)
 
 
-def scale_stored(a, dtype, factor):
-    """Multiply stored values by a power of two (exact in every format)."""
-    return S.to_storage((S.to_f64(a, dtype) * factor).astype(np.float32), dtype)
-
-
 def run_prefill_case(label, shape, act, kv, batch, tokens, start_pos, s_max, seed,
-                     out_rows=None, x_scale=1.0):
+                     out_rows=None, x_scale=1.0, gpu_edit=None):
     say(f"[{label}] prefill B={batch} T={tokens} start={start_pos} s_max={s_max} {act}/{kv} "
         f"x*{x_scale} {shape}")
     stored = random_layer(shape, act, seed)
@@ -36,7 +31,8 @@ def run_prefill_case(label, shape, act, kv, batch, tokens, start_pos, s_max, see
                                 act, kv, start_pos)
     if x_scale != 1.0:
         inp["x"] = scale_stored(inp["x"], act, x_scale)
-    dl = DeviceLayer(shape, stored, act, kv, max_pos=s_max)
+    # gpu_edit(stored) -> the weights the GPU gets instead (negative controls)
+    dl = DeviceLayer(shape, gpu_edit(stored) if gpu_edit else stored, act, kv, max_pos=s_max)
     x = to_dev(inp["x"], act)
     kc = to_dev(inp["k_cache"], kv)
     vc = to_dev(inp["v_cache"], kv)
@@ -66,7 +62,8 @@ def run_prefill_case(label, shape, act, kv, batch, tokens, start_pos, s_max, see
     return errs
 
 
-def run_decode_case(label, shape, act, kv, ctx_len, s_max, seed, x_scale=1.0, ntk_scale=None):
+def run_decode_case(label, shape, act, kv, ctx_len, s_max, seed, x_scale=1.0, ntk_scale=None,
+                    gpu_edit=None):
     batch = len(ctx_len)
     say(f"[{label}] decode B={batch} ctx={[int(c) for c in ctx_len][:8]} s_max={s_max} "
         f"{act}/{kv} x*{x_scale} ntk={ntk_scale} {shape}")
@@ -76,7 +73,8 @@ def run_decode_case(label, shape, act, kv, ctx_len, s_max, seed, x_scale=1.0, nt
     if x_scale != 1.0:
         inp["x"] = scale_stored(inp["x"], act, x_scale)
     ctx = np.asarray(ctx_len, dtype=np.int32)
-    dl = DeviceLayer(shape, stored, act, kv, max_pos=s_max, ntk_scale=ntk_scale)
+    dl = DeviceLayer(shape, gpu_edit(stored) if gpu_edit else stored, act, kv, max_pos=s_max,
+                     ntk_scale=ntk_scale)
     x = to_dev(inp["x"], act)
     kc = to_dev(inp["k_cache"], kv)
     vc = to_dev(inp["v_cache"], kv)
@@ -371,13 +369,16 @@ def test_prefill_13b_full_sampled_rows():
 # Tiny stack: greedy ids
 # ---------------------------------------------------------------------------
 
-def test_tiny_stack_greedy_ids():
+@pytest.mark.parametrize("learned_gains", [False, True], ids=["unit-gains", "learned-gains"])
+def test_tiny_stack_greedy_ids(learned_gains):
+    """The tiny fp32 stack as specified (every gain 1), and the same stack with
+    learned gains in both norms of each layer and in the final norm."""
     from llama2_decoder_layer_amd import binding as B
     from llama2_decoder_layer_amd.stack import Stack
     wl = S.WORKLOADS["tiny_stack_f32"]
-    st = S.draw_stack(wl)
+    st = S.draw_stack(wl, learned_gains=learned_gains)
     act = wl.act_dtype
-    say("[tiny-stack] generate on GPU")
+    say(f"[tiny-stack] generate on GPU (learned gains: {learned_gains})")
     layers = [DeviceLayer(wl.shape, lw, act, wl.kv_dtype, max_pos=wl.s_max) for lw in st["layers"]]
     stack = Stack(layers[0].cfg, [l.weights for l in layers], to_dev(st["embed"], act),
                   to_dev(st["final_norm"], act), to_dev(st["w_lm"], act), wl.vocab)
@@ -398,3 +399,96 @@ def test_tiny_stack_greedy_ids():
     assert err < TOL[act]
     assert gap.min() > 10 * TOL[act], "near-tie: ids cannot be compared"
     assert list(ids) == list(want_ids)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm gains: negative controls and the f16 range
+# ---------------------------------------------------------------------------
+
+def _ones_like_gain(g, act):
+    return S.to_storage(np.ones(g.shape, np.float32), act)
+
+
+GAIN_PATHS = {
+    # label: (runner, args) -- which kernels apply the gains
+    "decode1-bf16-fused": ("decode", S.Shape(512, 8, 2, 128, 1376), "bf16", "bf16", [100], 256),
+    "decode3-f32-fused": ("decode", S.Shape(256, 4, 2, 64, 688), "f32", "f32", [5, 60, 9], 64),
+    "decode2-f16-fused": ("decode", S.Shape(256, 4, 4, 64, 768), "f16", "f16", [10, 129], 160),
+    "decode7-bf16-normpass": ("decode", S.Shape(512, 8, 2, 128, 1376), "bf16", "f16",
+                              [0, 1, 63, 64, 65, 300, 200], 512),
+    "prefill64-bf16-wide": ("prefill", S.Shape(256, 4, 2, 64, 688), "bf16", "bf16", 64, 64),
+}
+
+
+def _run_gain_path(label, edit=None):
+    kind, shape, act, kv, arg, s_max = GAIN_PATHS[label]
+    gpu_edit = None
+    if edit == "ones":
+        def gpu_edit(st):
+            d = dict(st)
+            d["attn_norm"] = _ones_like_gain(st["attn_norm"], act)
+            d["ffn_norm"] = _ones_like_gain(st["ffn_norm"], act)
+            return d
+    elif edit == "swap":
+        def gpu_edit(st):
+            d = dict(st)
+            d["attn_norm"], d["ffn_norm"] = st["ffn_norm"], st["attn_norm"]
+            return d
+    tag = f"{label}-{edit or 'as-drawn'}"
+    if kind == "decode":
+        run_decode_case(tag, shape, act, kv, arg, s_max, 170, gpu_edit=gpu_edit)
+    else:
+        run_prefill_case(tag, shape, act, kv, 1, arg, 0, s_max, 170, gpu_edit=gpu_edit)
+
+
+@pytest.mark.parametrize("label", sorted(GAIN_PATHS))
+def test_learned_gains(label):
+    """Learned attn_norm and ffn_norm gains (different draws) on each path
+    that applies them: the fused staging of the row kernels (bf16, f16, f32),
+    the separate norm pass of the streaming projections, the prefill norms."""
+    _run_gain_path(label)
+
+
+@pytest.mark.parametrize("edit", ["ones", "swap"])
+@pytest.mark.parametrize("label", sorted(GAIN_PATHS))
+def test_learned_gains_negative_control(label, edit):
+    """The same cases with the GPU given unit gains, or attn_norm and ffn_norm
+    swapped, while the oracle keeps the drawn ones: the comparison must fail,
+    so the passing cases above do test the gains."""
+    with pytest.raises(AssertionError, match="errors above"):
+        _run_gain_path(label, edit)
+
+
+@pytest.mark.parametrize("batch", [1, 7])
+def test_f16_large_activation_with_gain(batch):
+    """f16 activations with an outlier of 30000 in x and gains up to 4: x times
+    the gain (120000) is beyond f16's range, the normalised row is not.  Both
+    the fused staging (1 token) and the norm pass (7 tokens) stay finite and
+    match the oracle."""
+    shape, act, kv = S.Shape(256, 4, 4, 64, 768), "f16", "f16"
+    s_max = 64
+    stored = random_layer(shape, act, 171)
+    g = S.to_f64(stored["attn_norm"], act)
+    g[3] = 4.0
+    stored["attn_norm"] = S.to_storage(g.astype(np.float32), act)
+    g2 = S.to_f64(stored["ffn_norm"], act)
+    g2[3] = 4.0
+    stored["ffn_norm"] = S.to_storage(g2.astype(np.float32), act)
+    inp = S.draw_decode_inputs(np.random.SeedSequence(172), shape, batch, s_max, act, kv, ctx=0)
+    x = S.to_f64(inp["x"], act)
+    x[:, 3] = 30000.0
+    inp["x"] = S.to_storage(x.astype(np.float32), act)
+    ctx = np.arange(batch, dtype=np.int32) * 7 + 3
+    say(f"[f16-outlier B={batch}] decode")
+    dl = DeviceLayer(shape, stored, act, kv, max_pos=s_max)
+    xd = to_dev(inp["x"], act)
+    kc, vc = to_dev(inp["k_cache"], kv), to_dev(inp["v_cache"], kv)
+    y = dl.decode(xd, kc, vc, torch.from_numpy(ctx).cuda(), batch, int(ctx.max()), s_max)
+    torch.cuda.synchronize()
+    got = from_dev(y)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    want = R.layer_decode(oracle_cfg(shape), oracle_weights(stored, act), x,
+                          S.to_f64(inp["k_cache"], kv), S.to_f64(inp["v_cache"], kv), ctx)
+    d_err, d_allow = delta_error(got, want, x, act)
+    check_errors(f"f16-outlier-B{batch}", {"out": rel_err(got, want), "delta": d_err}, TOL[act],
+                 {"delta": d_allow})

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from gpu_util import (TOL, check_errors, delta_error, from_dev, oracle_cfg, random_layer,
-                      rel_err, to_dev)
+                      rel_err, scale_stored, to_dev)
 from llama2_decoder_layer_amd import binding as B
 from llama2_decoder_layer_amd import synth as S
 from oracle import llama_ref as R
@@ -69,7 +69,8 @@ def oracle_w4_weights(stored, act):
     return R.LayerWeights(**out)
 
 
-def run_w4_decode(label, shape, act, kv, ctx_len, s_max, seed, stored=None, inp=None):
+def run_w4_decode(label, shape, act, kv, ctx_len, s_max, seed, stored=None, inp=None,
+                  x_scale=1.0):
     batch = len(ctx_len)
     say(f"[{label}] w4 decode B={batch} ctx={[int(c) for c in ctx_len][:8]} s_max={s_max} "
         f"{act}/{kv} {shape}")
@@ -78,6 +79,8 @@ def run_w4_decode(label, shape, act, kv, ctx_len, s_max, seed, stored=None, inp=
     if inp is None:
         inp = S.draw_decode_inputs(np.random.SeedSequence(seed + 1), shape, batch, s_max, act, kv,
                                    ctx=0)
+    if x_scale != 1.0:
+        inp = dict(inp, x=scale_stored(inp["x"], act, x_scale))
     ctx = np.asarray(ctx_len, dtype=np.int32)
     lw = device_w4_layer(shape, stored, act, s_max)
     cfg = B.make_config(shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim,
@@ -150,3 +153,11 @@ def test_w4_decode_7b_full():
     stored, inp = S.workload_layer_and_inputs(name)
     run_w4_decode(name, wl.shape, wl.act_dtype, wl.kv_dtype, list(inp["ctx_len"]), wl.s_max, 0,
                   stored=stored, inp=inp)
+
+
+@pytest.mark.parametrize("ctx", [[77], [5, 200, 33]], ids=["1-token", "3-tokens"])
+def test_w4_decode_branch_dominant(ctx):
+    """x scaled by 2^-8: the branches dominate the output, so the output
+    tolerance checks the quantised projections with no rounding allowance."""
+    run_w4_decode("w4-small-x-" + str(len(ctx)), S.Shape(512, 8, 2, 128, 1376), "bf16", "bf16", ctx,
+                  256, 185, x_scale=2.0 ** -8)

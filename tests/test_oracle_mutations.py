@@ -170,7 +170,58 @@ def _w8_generic(levels=127.0, rounding=np.rint, per_column=False, clip=127):
     return quant
 
 
+def _lm_head_no_final_norm(h, final_norm, w_lm, eps):
+    return np.asarray(h, F64) @ np.asarray(w_lm, F64).T
+
+
+def _lm_head_eps_outside(h, final_norm, w_lm, eps):
+    h = np.asarray(h, F64)
+    u = h / (np.sqrt(np.mean(h * h, axis=-1, keepdims=True)) + eps) * final_norm
+    return u @ np.asarray(w_lm, F64).T
+
+
+def _lm_head_no_gain(h, final_norm, w_lm, eps):
+    h = np.asarray(h, F64)
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps) @ np.asarray(w_lm, F64).T
+
+
+def _generate_generic(tied=False, first_position=False):
+    """generate_greedy with the head tied to the embedding table, or applied to
+    the prompt's first position instead of its last."""
+    def gen(cfg, layers, embed_table, final_norm, w_lm, prompt_ids, n_new, s_max):
+        head_w = embed_table if tied else w_lm
+        prompt_ids = np.asarray(prompt_ids, dtype=np.int64)
+        T = prompt_ids.shape[0]
+        caches = [(np.zeros((1, cfg.n_kv_heads, s_max, cfg.head_dim)),
+                   np.zeros((1, cfg.n_kv_heads, s_max, cfg.head_dim))) for _ in layers]
+        h = R.embed(embed_table, prompt_ids)[None]
+        for w, (kc, vc) in zip(layers, caches):
+            h = R.layer_prefill(cfg, w, h, kc, vc, 0)
+        logits = [R.lm_head(h[0, 0 if first_position else -1], final_norm, head_w, cfg.eps)]
+        ids = [int(R.greedy(logits[-1]))]
+        for step in range(n_new):
+            h = R.embed(embed_table, [ids[-1]])
+            ctx = np.array([T + step])
+            for w, (kc, vc) in zip(layers, caches):
+                h = R.layer_decode(cfg, w, h, kc, vc, ctx)
+            logits.append(R.lm_head(h[0], final_norm, head_w, cfg.eps))
+            ids.append(int(R.greedy(logits[-1])))
+        return np.array(ids), np.stack(logits)
+    return gen
+
+
+def _embed_off_by_one(table, ids):
+    t = np.asarray(table, F64)
+    return t[(np.asarray(ids, dtype=np.int64) + 1) % t.shape[0]]
+
+
 MUTANTS = {
+    "lm_head_drops_final_norm": ("lm_head", _lm_head_no_final_norm),
+    "lm_head_eps_outside_sqrt": ("lm_head", _lm_head_eps_outside),
+    "lm_head_drops_gain": ("lm_head", _lm_head_no_gain),
+    "generate_tied_head": ("generate_greedy", _generate_generic(tied=True)),
+    "generate_head_on_first_position": ("generate_greedy", _generate_generic(first_position=True)),
+    "embed_off_by_one": ("embed", _embed_off_by_one),
     "rmsnorm_eps_outside_sqrt": ("rmsnorm", _rmsnorm_eps_outside),
     "rmsnorm_drops_gamma": ("rmsnorm", _rmsnorm_no_gamma),
     "rmsnorm_across_tokens": ("rmsnorm", _rmsnorm_across_tokens),
