@@ -62,7 +62,8 @@ enum {
   LL_ECACHE_FULL = -4,  /* positions would run past the cache capacity s_max */
   LL_EWORKSPACE = -5,   /* workspace missing or smaller than required        */
   LL_EHIP = -6,         /* the HIP runtime reported an error at launch       */
-  LL_EUNSUPPORTED = -7  /* valid but not implemented (e.g. head_dim 96)      */
+  LL_EUNSUPPORTED = -7, /* valid but not implemented (e.g. head_dim 96)      */
+  LL_ESCRATCH = -8      /* llama_layer_decode_noalloc: call exceeds its scratch */
 };
 
 /*
@@ -141,6 +142,26 @@ int llama_layer_prefill(const ll_config* cfg, const ll_weights* w, const void* x
 int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
                        void* k_cache, void* v_cache, const int32_t* ctx_len, int32_t batch,
                        int32_t max_ctx, int32_t s_max, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * llama_layer_decode without a workspace argument and without allocating, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, caches,
+ * results and errors as llama_layer_decode (the same kernels, bit-identical
+ * outputs).  The workspace is a built-in device array of 64 MiB, one per
+ * device, held from the library's first use on that device until the process
+ * ends; its address is looked up on the first call on each device.  A call
+ * whose workspace, sized for its batch and max_ctx, exceeds 64 MiB returns
+ * LL_ESCRATCH before enqueueing anything (e.g. 7B-shaped layers: batch 1 up to
+ * 32K contexts; 70B-shaped: batch 32 at 4K).  Every call on a device shares
+ * that device's array, so calls that can overlap on one device (different
+ * streams, several host threads) race: order them.  The array keeps the last
+ * call's contents; the decode needs none of it to start at zero.  Never
+ * allocates, frees or synchronises.
+ */
+int llama_layer_decode_noalloc(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                               void* k_cache, void* v_cache, const int32_t* ctx_len,
+                               int32_t batch, int32_t max_ctx, int32_t s_max, void* stream);
 
 /*
  * Paged KV cache ("Llama2架构全景解析" §2.3 and §3.1: paging the KV cache ends

@@ -22,7 +22,7 @@ DTYPE_CODE = {"f32": LL_F32, "bf16": LL_BF16, "f16": LL_F16,
 TORCH_DTYPE = {LL_F32: torch.float32, LL_BF16: torch.bfloat16, LL_F16: torch.float16}
 
 ERRORS = {0: "LL_OK", -1: "LL_EINVAL", -2: "LL_ENULL", -3: "LL_EALIGN", -4: "LL_ECACHE_FULL",
-          -5: "LL_EWORKSPACE", -6: "LL_EHIP", -7: "LL_EUNSUPPORTED"}
+          -5: "LL_EWORKSPACE", -6: "LL_EHIP", -7: "LL_EUNSUPPORTED", -8: "LL_ESCRATCH"}
 
 
 class LlamaLayerError(RuntimeError):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.llama_layer_prefill.restype = ctypes.c_int
         L.llama_layer_decode.argtypes = [CP, WP, P, P, P, P, P, I32, I32, I32, P, SZ, P]
         L.llama_layer_decode.restype = ctypes.c_int
+        L.llama_layer_decode_noalloc.argtypes = [CP, WP, P, P, P, P, P, I32, I32, I32, P]
+        L.llama_layer_decode_noalloc.restype = ctypes.c_int
         L.llama_rope_table.argtypes = [P, P, I32, I32, F, P]
         L.llama_rope_table.restype = ctypes.c_int
         L.llama_rope_table_ntk.argtypes = [P, P, I32, I32, F, F, P]
@@ -183,6 +185,16 @@ def llama_layer_decode(cfg, weights: LayerWeights, x, y, k_cache, v_cache, ctx_l
                                   _ptr(y), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), batch,
                                   max_ctx, s_max, _ptr(ws), nbytes, _stream(stream))
     _check(rc, "llama_layer_decode")
+
+
+def llama_layer_decode_noalloc(cfg, weights: LayerWeights, x, y, k_cache, v_cache, ctx_len, batch,
+                               max_ctx, s_max, stream=None) -> None:
+    """llama_layer_decode with the library's built-in device scratch (no
+    workspace argument, nothing allocated)."""
+    rc = lib().llama_layer_decode_noalloc(ctypes.byref(cfg), ctypes.byref(weights.struct), _ptr(x),
+                                          _ptr(y), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+                                          batch, max_ctx, s_max, _stream(stream))
+    _check(rc, "llama_layer_decode_noalloc")
 
 
 class LayerWeightsW8:

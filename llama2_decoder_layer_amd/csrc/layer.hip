@@ -126,7 +126,8 @@ struct Layout {
   int nsplit_max;
 };
 
-static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide) {
+// nsplit_max < 0: room for the attention splits of any context up to s_max.
+static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide, int nsplit_max = -1) {
   Layout L{};
   const size_t act = esize(c->act_dtype);
   const size_t qd = (size_t)c->n_heads * c->head_dim;
@@ -147,7 +148,7 @@ static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide) {
     // Token-skinny plans process at most 32 tokens at a time.
     const int64_t g = std::min<int64_t>(bt, 32);
     const int cmin = attn_min_chunk(c->head_dim);
-    L.nsplit_max = (s_max + cmin - 1) / cmin;
+    L.nsplit_max = nsplit_max >= 0 ? nsplit_max : (s_max + cmin - 1) / cmin;
     L.u = take(g * c->hidden * act);   // norm pre-pass when the LDS stage is too small
     L.q32 = take(g * qd * 4);
     L.pm = take(g * c->n_heads * L.nsplit_max * 4);
@@ -496,12 +497,85 @@ int llama_layer_decode(const ll_config* cfg, const ll_weights* w, const void* x,
   return LL_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free decode.  The workspace is a file-scope device array, one
+// copy per device (the loader places it with the code object; it lives until
+// the process ends).  Host code never passes `scratch` itself to a kernel:
+// that name is a host-side stand-in.  Its device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static std::vector<uint8_t*> g_scratch_dev;  // device index -> address of `scratch`
+
+static int scratch_address(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LL_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_dev.size()) g_scratch_dev.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LL_EHIP;
+    g_scratch_dev[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch_dev[dev];
+  return LL_OK;
+}
+
+// Attention splits a decode of `batch` sequences needs at contexts up to
+// max_ctx: the largest over the launch groups it runs (32 sequences, then the
+// rest), with the chunk each group's launch picks.
+static int decode_nsplit_need(const ll_config* c, int batch, int max_ctx) {
+  const int max_keys = max_ctx + 1, g = c->n_heads / c->n_kv_heads;
+  int need = 0;
+  for (int m : {std::min(batch, 32), batch % 32}) {
+    if (m <= 0) continue;
+    const int chunk = attn_pick_chunk(c->head_dim, max_keys, m, c->n_kv_heads, g, c->kv_dtype);
+    if (chunk <= 0) return -1;
+    need = std::max(need, (max_keys + chunk - 1) / chunk);
+  }
+  return need;
+}
+
 static int check_pages(int32_t n_blocks, int32_t max_blocks, int32_t block_size, int* log2_bs) {
   if (n_blocks <= 0 || max_blocks <= 0) return LL_EINVAL;
   int l = 0;
   while ((1 << l) < block_size && l < 30) ++l;
   if (block_size < 16 || block_size > 1024 || (1 << l) != block_size) return LL_EINVAL;
   *log2_bs = l;
+  return LL_OK;
+}
+
+int llama_layer_decode_noalloc(const ll_config* cfg, const ll_weights* w, const void* x, void* y,
+                               void* k_cache, void* v_cache, const int32_t* ctx_len,
+                               int32_t batch, int32_t max_ctx, int32_t s_max, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if ((rc = check_ptrs({x, y, k_cache, v_cache}))) return rc;
+  if ((rc = check_ptrs4({ctx_len}))) return rc;
+  if (batch <= 0 || max_ctx < 0 || s_max <= 0) return LL_EINVAL;
+  if ((int64_t)max_ctx + 1 > s_max || (int64_t)max_ctx + 1 > cfg->max_pos) return LL_ECACHE_FULL;
+  const size_t act = esize(cfg->act_dtype);
+  if (overlap(x, (size_t)batch * cfg->hidden * act, y, (size_t)batch * cfg->hidden * act))
+    return LL_EINVAL;
+  const int nsplit = decode_nsplit_need(cfg, batch, max_ctx);
+  if (nsplit < 0) return LL_EUNSUPPORTED;
+  // Sized for this call's contexts, not for s_max.
+  const Layout L = layout(cfg, batch, s_max, false, nsplit);
+  if (L.total > NOALLOC_SCRATCH_BYTES) return LL_ESCRATCH;
+  uint8_t* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  for (int b0 = 0; b0 < batch; b0 += 32) {
+    const int m = std::min(32, batch - b0);
+    rc = run_skinny(cfg, w, nullptr, x, y, k_cache, v_cache, ctx_len, 0, 1, max_ctx, s_max, b0,
+                    m, ws, L, s);
+    if (rc) return rc;
+  }
   return LL_OK;
 }
 
@@ -822,6 +896,9 @@ const char* llama_layer_strerror(int code) {
     case LL_EWORKSPACE: return "workspace missing or too small";
     case LL_EHIP: return "HIP launch error";
     case LL_EUNSUPPORTED: return "configuration not supported (head_dim must be 64 or 128)";
+    case LL_ESCRATCH:
+      return "the call needs more workspace than the 64 MiB built-in scratch of "
+             "llama_layer_decode_noalloc (use llama_layer_decode with a workspace)";
   }
   return "unknown error";
 }

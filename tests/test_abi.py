@@ -38,7 +38,7 @@ def test_one_hip_runtime_in_process():
 
 def test_strerror():
     assert B.llama_layer_strerror(0) == "ok"
-    for code in range(-7, 0):
+    for code in range(-8, 0):
         assert B.llama_layer_strerror(code) != "unknown error"
     assert B.llama_layer_strerror(-99) == "unknown error"
 
@@ -300,3 +300,29 @@ def test_w4_decode_validation():
     assert rc(c=cfg(intermediate=688)) == -1             # not a multiple of 32
     assert B.lib().llama_layer_decode_w4(ctypes.byref(c), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1,
                                          32, FAKE, 1, None) == -2
+
+
+def test_noalloc_validation():
+    """llama_layer_decode_noalloc validates like llama_layer_decode, and refuses
+    a call whose workspace would exceed its built-in scratch with LL_ESCRATCH
+    before touching the device."""
+    L = B.lib()
+
+    def rc(c, batch=1, max_ctx=8, s_max=32, x=FAKE, y=FAKE + 0x100000, ctx=FAKE + 0x600000):
+        return L.llama_layer_decode_noalloc(ctypes.byref(c), ctypes.byref(weights().struct), x, y,
+                                            FAKE + 0x200000, FAKE + 0x300000, ctx, batch, max_ctx,
+                                            s_max, None)
+
+    c = cfg()
+    assert rc(c, batch=0) == -1
+    assert rc(c, max_ctx=-1) == -1
+    assert rc(c, max_ctx=32, s_max=32) == -4
+    assert rc(c, y=FAKE + 16) == -1                    # y overlaps x
+    assert rc(c, ctx=FAKE + 0x600002) == -3
+    assert rc(c, x=None) == -2
+    assert L.llama_layer_decode_noalloc(None, ctypes.byref(weights().struct), FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, 1, 8, 32, None) == -2
+    big = cfg(hidden=8192, n_heads=64, n_kv_heads=8, head_dim=128, intermediate=28672,
+              max_pos=8192)
+    assert rc(big, batch=1024, max_ctx=4096, s_max=4097, y=FAKE + 0x10000000) == -8
+    assert "64 MiB" in B.llama_layer_strerror(-8)
