@@ -1,11 +1,17 @@
 """Benchmark of the decoder layer on one MI355X.
 
-A step is one call of the layer (every step of the hot path) on one batch of
-seeded synthetic input already resident in HBM.  The default workload is the
-7B-shaped layer decoding one token against a 4096-position cache; the JSON line
-also carries the layer's algorithmic HBM rate, the roofline of its dominant
-kernel (timed with HIP events around that kernel's launches on its stream, over
-the timed steps) and the fp64 oracle timed on the host's cores.
+Default workload: the 80-layer 70B-shaped stack at batch 1 (1024-token prompt,
+then greedy decode).  A step is one decode token through every layer and the
+LM head; value = decode tokens/s over exactly --steps steps timed between
+synchronisations.  The line also carries the median step, the stack's
+algorithmic HBM rate, the prompt prefill's time to first token and TFLOP/s
+(median of --prefills runs), the roofline of the dominant decode kernel (the
+gate/up GEMV, timed with HIP events handed to its dispatches), HBM read/copy and
+bf16 MFMA rates measured on the GPU beside the published peaks, and the fp64
+oracle timed on the host's cores (an extrapolation from one layer).
+
+--workload selects a single-layer workload instead (a step is one layer call;
+decode: tokens/s per layer; prefill: TFLOP/s) or the sampling head.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -167,13 +173,78 @@ def cpu_baseline_stack(wl, drawn, budget_s: float) -> dict:
                       f"({t_head * 1e3:.0f} ms)"}
 
 
+def median(xs):
+    return float(np.median(np.asarray(xs, dtype=np.float64)))
+
+
+class StepEvents:
+    """HIP events on torch's current stream (the stream the library launches
+    on) between consecutive steps, for the median step time."""
+
+    def __init__(self, n):
+        import torch
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        self.i = 0
+
+    def mark(self):
+        self.ev[self.i].record()
+        self.i += 1
+
+    def times_ms(self):
+        return [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(self.i - 1)]
+
+
+def measured_peaks() -> dict:
+    """HBM read and copy rates and the bf16 MFMA rate measured on this GPU with
+    the library's peak kernels (median of 5 runs each), beside the published
+    peaks the roofline fractions use."""
+    import torch
+    from llama2_decoder_layer_amd import binding as B
+    gib = 1 << 30
+    src = torch.ones(4 * gib // 4, dtype=torch.int32, device="cuda")   # 4 GiB >> the 256 MB MALL
+    dst = torch.empty(2 * gib // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    out = torch.empty(131072, dtype=torch.float32, device="cuda")
+
+    def timed(fn, n=5):
+        fn()  # warm
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return median(ts)
+
+    read_ms = timed(lambda: B.llama_peak_read(src, sink))
+    copy_ms = timed(lambda: B.llama_peak_copy(dst, src[:dst.numel()]))
+    iters = 4096
+    flops = B.llama_peak_mfma_bf16(out, iters)
+    torch.cuda.synchronize()
+    mfma_ms = timed(lambda: B.llama_peak_mfma_bf16(out, iters))
+    res = {"hbm_read_GBps": 4 * gib / (read_ms / 1e3) / 1e9,
+           "hbm_copy_GBps": 2 * 2 * gib / (copy_ms / 1e3) / 1e9,
+           "mfma_bf16_TFLOPs": flops / (mfma_ms / 1e3) / 1e12,
+           "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_mfma_bf16_TFLOPs": BF16_PEAK_TFLOPS,
+           "how": "llama_peak_read (4 GiB), llama_peak_copy (2 GiB each way), "
+                  "llama_peak_mfma_bf16 (32x32x16 bf16 chains on registers); median of 5"}
+    del src, dst, sink, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_stack(args, wl):
-    """The 80-layer stack at batch 1: a warm-up generation (prefill and `warmup`
-    decode steps), then a fresh generation whose prefill (time to first token)
-    and first `steps` decode steps are timed.  value = decode tokens/s."""
+    """The 80-layer stack at batch 1.  A warm-up generation (prefill and `warmup`
+    decode steps); then the prompt's prefill `--prefills` times (time to first
+    token: the median), then exactly `steps` decode steps, timed between
+    synchronisations (value = decode tokens/s) with an event between steps
+    (the median step)."""
     import torch
     from llama2_decoder_layer_amd import binding as B
     from llama2_decoder_layer_amd import synth as S
+    from llama2_decoder_layer_amd.profiling import load_traffic
     from llama2_decoder_layer_amd.stack import device_stack
     s = wl.shape
     steps = min(args.steps, wl.new_tokens)
@@ -191,19 +262,30 @@ def bench_stack(args, wl):
     del g
     g = stack.begin(prompt, wl.new_tokens, wl.s_max)
     torch.cuda.synchronize()
-    print(f"[bench] timing prefill + {steps} decode steps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    g.prefill()
-    torch.cuda.synchronize()
-    t_prefill = time.perf_counter() - t0
+    print(f"[bench] timing {args.prefills} prefills", file=sys.stderr, flush=True)
+    pre_ms = []
+    for _ in range(args.prefills):  # idempotent: rewrites the prompt's cache entries
+        ev = StepEvents(1)
+        ev.mark()
+        g.prefill()
+        ev.mark()
+        torch.cuda.synchronize()
+        pre_ms += ev.times_ms()
+    t_prefill = median(pre_ms) / 1e3
+    print(f"[bench] timing {steps} decode steps", file=sys.stderr, flush=True)
     kid = B.kernel_id("gemv_gate_up")
     B.llama_layer_timer_start(kid, wl.n_layers * steps)
+    ev = StepEvents(steps)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        ev.mark()
         g.decode(i)
+    ev.mark()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     kms, kn = B.llama_layer_timer_stop()
+    step_ms = ev.times_ms()
     ms_tok = el * 1e3 / steps
     act_b = S.DTYPE_BYTES[wl.act_dtype]
     kv_b = S.DTYPE_BYTES[wl.kv_dtype]
@@ -215,18 +297,21 @@ def bench_stack(args, wl):
     kavg_s = kms / 1e3 / max(kn, 1)
     ach = per_layer["gemv_gate_up"] / kavg_s / 1e9
     fl = wl.n_layers * prefill_flops(s, wl.prompt)["total"]
+    tr = load_traffic("gemv_gate_up", wl.name)
     out = {"metric": METRIC, "value": steps / el, "unit": "tokens/s", "n_gpus": 1,
-           "steps": steps, "warmup": warm, "ms_per_step": ms_tok, "higher_is_better": True,
+           "steps": steps, "warmup": warm, "ms_per_step": ms_tok,
+           "ms_per_step_median": median(step_ms), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": wl.act_dtype,
            "data": "synthetic (device-drawn seeded weights; see synth.py)",
+           "layer_steps_per_s": wl.n_layers * steps / el,
            "stack_hbm": {"bytes_per_token": int(tok_bytes), "GBps": gbps,
                          "frac_of_peak": gbps / HBM_PEAK_GBPS},
            "prefill": {"tokens": wl.prompt, "time_to_first_token_ms": t_prefill * 1e3,
-                       "flops": fl, "TFLOPs": fl / t_prefill / 1e12,
+                       "runs_ms": pre_ms, "flops": fl, "TFLOPs": fl / t_prefill / 1e12,
                        "frac_of_peak": fl / t_prefill / 1e12 / BF16_PEAK_TFLOPS},
            "roofline": {"bound": "hbm", "kernel": "gemv_gate_up", "achieved": ach,
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
-                        "traffic": None,
+                        "traffic": None if tr is None else tr["bytes"],
                         "algorithmic_bytes_per_launch": per_layer["gemv_gate_up"],
                         "avg_launch_us": kavg_s * 1e6, "launches_timed": kn},
            "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": s.hidden,
@@ -234,12 +319,30 @@ def bench_stack(args, wl):
                       "intermediate": s.intermediate, "vocab": wl.vocab, "batch": 1,
                       "prompt": wl.prompt, "kv_dtype": wl.kv_dtype},
            "ids_head": [int(i) for i in g.ids[:8].cpu()]}
+    del g
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+    if not args.no_peaks:
+        print("[bench] measuring HBM and MFMA peaks", file=sys.stderr, flush=True)
+        out["measured_peaks"] = measured_peaks()
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_stack(wl, drawn, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(mib: int) -> None:
+    """Three device-to-device copies of `mib` MiB: the known-size reference
+    that scales the HBM byte counters of a counter run."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def paged_pools(inp, bs, seed):
@@ -291,12 +394,7 @@ def bench_sample(args, wl):
     ms_step = el * 1e3 / args.steps
     kavg_s = kms / 1e3 / max(kn, 1)
     if args.copy_calibration:
-        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(args.copy_calibration)
     nbytes = wl.batch * (wl.vocab * 4 + e["n_hist"] * 4 + 4 + 4)
     from llama2_decoder_layer_amd.profiling import load_traffic
     tr = load_traffic("sample", wl.name)
@@ -334,9 +432,11 @@ def bench_sample(args, wl):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_7b_b1_ctx4096",
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 32 decode tokens for the stack, 200 layer calls)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 4 for the stack, 20 layer calls)")
+    ap.add_argument("--workload", default="stack_70b_80l",
                     choices=["decode_7b_b1_ctx4096", "decode_70b_b32_ragged", "prefill_13b_t4096",
                              "stack_70b_80l", "decode_7b_b1_ctx32768_ntk8",
                              "sample_b32_v32000", "decode_7b_b1_ctx4096_w8",
@@ -346,10 +446,19 @@ def main():
                     help="distinct weight/cache copies cycled through (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured HBM/MFMA peaks (stack workload)")
+    ap.add_argument("--prefills", type=int, default=3,
+                    help="stack workload: prompt prefills timed (time to first token: median)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run 3 device-to-device copies of MIB MiB (the "
                          "known-size reference that scales the HBM byte counters)")
     args = ap.parse_args()
+    stack_wl = args.workload == "stack_70b_80l"
+    if args.steps is None:
+        args.steps = 32 if stack_wl else 200
+    if args.warmup is None:
+        args.warmup = 4 if stack_wl else 20
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -469,24 +578,23 @@ def main():
     kid = B.kernel_id(dom)
     B.llama_layer_timer_start(kid, args.steps)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev = StepEvents(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        ev.mark()
         step(i)
+    ev.mark()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     kms, kn = B.llama_layer_timer_stop()
     ms_step = el * 1e3 / args.steps
     if args.copy_calibration:
-        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(args.copy_calibration)
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "ms_per_step": ms_step, "ms_per_step_median": median(ev.times_ms()),
+           "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": act, "data": "synthetic (seeded; see synth.py)"}
     kavg_s = kms / 1e3 / max(kn, 1)
     # HBM bytes per launch of the dominant kernel from the committed counter

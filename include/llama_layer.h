@@ -411,6 +411,29 @@ int llama_layer_timer_stop(double* total_ms, int32_t* launches);
 /* Name of a kernel id, or NULL past the last one. */
 const char* llama_layer_kernel_name(int32_t kernel_id);
 
+/*
+ * Measured peaks (benchmark instrumentation, not part of the layer): the rates
+ * the layer's roofline fractions are read against, taken on the GPU in use,
+ * beside the published 8 TB/s HBM and 2.5 PFLOP/s dense bf16 MFMA.
+ *   llama_peak_read       streams `bytes` of src (DEVICE, 16-byte aligned,
+ *                         bytes a multiple of 16) once, non-temporal 16-byte
+ *                         loads; sink DEVICE uint32 [1024] is written only in
+ *                         the practically impossible case that the XOR of all
+ *                         the data equals a fixed constant (it keeps the loads
+ *                         live).
+ *   llama_peak_copy       copies `bytes` from src to dst (DEVICE, 16-byte
+ *                         aligned, not overlapping): bytes read + bytes written.
+ *   llama_peak_mfma_bf16  back-to-back v_mfma_f32_32x32x16_bf16 on register
+ *                         operands, no memory traffic; *flops (HOST) receives
+ *                         the work enqueued (iters * 2^28 FLOPs); out
+ *                         DEVICE float32 [131072] receives the sums.
+ * Time them with events on `stream`.  Errors: LL_ENULL, LL_EALIGN, LL_EINVAL,
+ * LL_EHIP.
+ */
+int llama_peak_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+int llama_peak_copy(void* dst, const void* src, size_t bytes, void* stream);
+int llama_peak_mfma_bf16(float* out, int32_t iters, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

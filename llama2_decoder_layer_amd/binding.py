@@ -107,6 +107,12 @@ def lib() -> ctypes.CDLL:
         L.llama_embed.restype = ctypes.c_int
         L.llama_head_argmax.argtypes = [P, P, P, P, P, I32, I32, I32, F, I32, P]
         L.llama_head_argmax.restype = ctypes.c_int
+        L.llama_peak_read.argtypes = [P, SZ, P, P]
+        L.llama_peak_read.restype = ctypes.c_int
+        L.llama_peak_copy.argtypes = [P, P, SZ, P]
+        L.llama_peak_copy.restype = ctypes.c_int
+        L.llama_peak_mfma_bf16.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), P]
+        L.llama_peak_mfma_bf16.restype = ctypes.c_int
         L.llama_layer_strerror.argtypes = [ctypes.c_int]
         L.llama_layer_strerror.restype = ctypes.c_char_p
         L.llama_layer_timer_start.argtypes = [I32, I32]
@@ -351,3 +357,21 @@ def kernel_id(name: str) -> int:
         if n == name:
             return i
         i += 1
+
+
+def llama_peak_read(src, sink, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    _check(lib().llama_peak_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "llama_peak_read")
+
+
+def llama_peak_copy(dst, src, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    _check(lib().llama_peak_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "llama_peak_copy")
+
+
+def llama_peak_mfma_bf16(out, iters: int, stream=None) -> float:
+    """Enqueues the MFMA loop; returns the FLOPs it performs."""
+    fl = ctypes.c_double()
+    _check(lib().llama_peak_mfma_bf16(_ptr(out), iters, ctypes.byref(fl), _stream(stream)),
+           "llama_peak_mfma_bf16")
+    return fl.value

@@ -502,51 +502,109 @@ void gemm_dma_kernel(ProjArgs a, float* part, int full_tiles, int ksplit) {
   };
 
   const int nkt = kt_end - kt_begin;
+  if constexpr (NST == 2) {
+    // Two 64-k stages.  Stage kt+1 streams into the other buffer while stage
+    // kt is multiplied, its DMA instructions spread between the MFMAs of the
+    // stage's first half (one per MPD MFMAs) instead of issued as a burst
+    // after the barrier: a burst of 8 x 1 KB per wave filled the vector-memory
+    // queue, and the in-order issue held every wave's next MFMAs behind it
+    // (13B gate/up 1190 -> 1139 us, 70B gate/up at 1024 tokens 1010 -> 981 us,
+    // on one box with alternating builds).  The stage then ends with this
+    // wave's DMA of stage kt+1 landed (vmcnt 0), all fragment reads of stage
+    // kt done, and the one barrier, after which stage kt+1's first fragments
+    // are read.
+    constexpr int NDMA = AI + BI;                       // DMA instructions per wave per stage
+    constexpr int MPD = (KS * RB * CB) / (2 * NDMA);    // MFMAs between two of them
+    static_assert(MPD >= 1 && NDMA * MPD <= KS * RB * CB / 2,
+                  "every DMA of a stage is issued before its sync point");
+    auto issue_one = [&](int st, int kt, int i) {
+      uint8_t* base = lds + st * STAGE;
+      const int k = (kt_begin + kt) * BK;
+      if (i < AI) dma16(asrc[i] + k, base + (wave * AI + i) * 1024);
+      else dma16(bsrc[i - AI] + k, base + BM * ROWB + (wave * BI + (i - AI)) * 1024);
+    };
+    issue(0, 0);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    read_set(ic<0>{}, 0, 0);
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int st = kt & 1;
+      const bool pre = kt + 1 < nkt;
+      static_for<0, KS>([&](auto KSI) {
+        constexpr int ks = decltype(KSI)::value;
+        constexpr int S = ks & 1;
+        static_for<0, RB * CB>([&](auto MI) {
+          constexpr int m = decltype(MI)::value;
+          constexpr int g = ks * RB * CB + m;  // MFMA index within the stage
+          __builtin_amdgcn_sched_barrier(0);
+          acc[m / CB][m % CB] = mfma32<DT>(fa[S][m / CB], fb[S][m % CB], acc[m / CB][m % CB]);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr ((g + 1) % MPD == 0 && (g + 1) / MPD <= NDMA) {
+            if (pre) issue_one(st ^ 1, kt + 1, (g + 1) / MPD - 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if constexpr (m == RB * CB / 2 - 1) {  // mid-step: the next step's fragments
+            if constexpr (ks + 1 < KS) {
+              read_set(ic<S ^ 1>{}, st, ks + 1);
+            } else {
+              // Unconditional (the last stage reads a valid buffer it never
+              // uses): a branch here makes the wait-count pass wait for these
+              // reads before the MFMAs that follow.
+              wait_lgkmcnt0();
+              wait_vmcnt<0>();
+              __builtin_amdgcn_s_barrier();
+              read_set(ic<S ^ 1>{}, st ^ 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
 #pragma unroll
-  for (int st = 0; st < NST; ++st)
-    if (st < nkt) issue(st, st);
-  wait_stage(min(NST, nkt) - 1);
-  __builtin_amdgcn_s_barrier();
-  read_set(ic<0>{}, 0, 0);
+    for (int st = 0; st < NST; ++st)
+      if (st < nkt) issue(st, st);
+    wait_stage(min(NST, nkt) - 1);
+    __builtin_amdgcn_s_barrier();
+    read_set(ic<0>{}, 0, 0);
 
-  // Per 16-k step: the first half of its MFMAs, then the reads of the next
-  // step, then the second half.  After the first half of a stage's last step
-  // (all of the stage read, the next stage landed everywhere) comes the one
-  // barrier of the stage; then the buffer just finished is refilled with stage
-  // kt+NST and the next stage's first step is read.  Barriers are bare
-  // s_barrier: the waits that make them safe are explicit.  The sched_barriers
-  // pin this order (the scheduler would otherwise sink each fragment read next
-  // to its first use).
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt % NST;
-    static_for<0, KS>([&](auto KSI) {
-      constexpr int ks = decltype(KSI)::value;
-      constexpr int S = ks & 1;
+    // Per 16-k step: the first half of its MFMAs, then the reads of the next
+    // step, then the second half.  After the first half of a stage's last step
+    // (all of the stage read, the next stage landed everywhere) comes the one
+    // barrier of the stage; then the buffer just finished is refilled with
+    // stage kt+NST and the next stage's first step is read.  Barriers are bare
+    // s_barrier: the waits that make them safe are explicit.  The
+    // sched_barriers pin this order (the scheduler would otherwise sink each
+    // fragment read next to its first use).
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int st = kt % NST;
+      static_for<0, KS>([&](auto KSI) {
+        constexpr int ks = decltype(KSI)::value;
+        constexpr int S = ks & 1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < RB / 2; ++r)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(fa[S][r], fb[S][c], acc[r][c]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks + 1 < KS) {
+          read_set(ic<S ^ 1>{}, st, ks + 1);
+        } else {
+          wait_lgkmcnt0();
+          wait_stage(max(min(kt + NST, nkt) - 1 - (kt + 1), 0));
+          __builtin_amdgcn_s_barrier();
+          if (kt + NST < nkt) issue(st, kt + NST);
+          read_set(ic<S ^ 1>{}, (kt + 1) % NST, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = RB / 2; r < RB; ++r)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(fa[S][r], fb[S][c], acc[r][c]);
+      });
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int r = 0; r < RB / 2; ++r)
-#pragma unroll
-        for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(fa[S][r], fb[S][c], acc[r][c]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (ks + 1 < KS) {
-        read_set(ic<S ^ 1>{}, st, ks + 1);
-      } else {
-        // Unconditional (the last stage reads a valid buffer it never uses): a
-        // branch here makes the wait-count pass wait for these reads before
-        // the MFMAs below.
-        wait_lgkmcnt0();
-        wait_stage(max(min(kt + NST, nkt) - 1 - (kt + 1), 0));
-        __builtin_amdgcn_s_barrier();
-        if (kt + NST < nkt) issue(st, kt + NST);
-        read_set(ic<S ^ 1>{}, (kt + 1) % NST, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int r = RB / 2; r < RB; ++r)
-#pragma unroll
-        for (int c = 0; c < CB; ++c) acc[r][c] = mfma32<DT>(fa[S][r], fb[S][c], acc[r][c]);
-    });
-    __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if (pidx >= 0) {  // one K part of a split tile: float32 partials, [part][quad][thread]
