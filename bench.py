@@ -448,6 +448,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured HBM/MFMA peaks (stack workload)")
+    ap.add_argument("--time-kernel", default=None, metavar="NAME",
+                    help="single-layer workloads: kernel the roofline block times (default: the "
+                         "dominant one; names as llama_layer_kernel_name)")
     ap.add_argument("--prefills", type=int, default=3,
                     help="stack workload: prompt prefills timed (time to first token: median)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -571,6 +574,8 @@ def main():
             B.llama_layer_prefill(cfg, lw, x, y, kc, vc, wl.batch, wl.tokens, 0, wl.s_max, ws)
         dom = "gemm_gate_up"
 
+    if args.time_kernel:
+        dom = args.time_kernel
     print(f"[bench] {copies} copies, warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
@@ -608,21 +613,24 @@ def main():
         layer_gbps = by["total"] / (ms_step / 1e3) / 1e9
         out["layer_hbm"] = {"bytes_per_step": by["total"], "GBps": layer_gbps,
                             "frac_of_peak": layer_gbps / HBM_PEAK_GBPS}
-        ach = by[dom] / kavg_s / 1e9
+        unit_bytes = by.get(dom)
+        ach = unit_bytes / kavg_s / 1e9 if unit_bytes else None
         out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
-                           "algorithmic_bytes_per_launch": by[dom], "avg_launch_us": kavg_s * 1e6,
-                           "launches_timed": kn}
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS if ach else None,
+                           "traffic": traffic, "algorithmic_bytes_per_launch": unit_bytes,
+                           "avg_launch_us": kavg_s * 1e6, "launches_timed": kn}
     else:
         fl = prefill_flops(s, wl.tokens)
         tflops = fl["total"] / (ms_step / 1e3) / 1e12
         out.update(value=tflops, unit="TFLOP/s")
         out["layer_mfma"] = {"flops_per_step": fl["total"], "TFLOPs": tflops,
                              "frac_of_peak": tflops / BF16_PEAK_TFLOPS}
-        ach = fl["gate_up"] / kavg_s / 1e12
+        unit_flops = fl[{"gemm_qkv": "qkv", "gemm_o": "o", "gemm_gate_up": "gate_up",
+                         "gemm_down": "down", "attn_prefill": "attention"}[dom]]
+        ach = unit_flops / kavg_s / 1e12
         out["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": traffic,
-                           "algorithmic_flops_per_launch": fl["gate_up"],
+                           "algorithmic_flops_per_launch": unit_flops,
                            "avg_launch_us": kavg_s * 1e6, "launches_timed": kn}
     out["config"] = {"workload": wl.name, "hidden": s.hidden, "n_heads": s.n_heads,
                      "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,

@@ -23,6 +23,7 @@ constexpr int VT_STRIDE = PKV + 4;  // padded row of the transposed V tile (elem
 // K/V tile stages in LDS (head_dim 128 kernel).  Two keep two workgroups per
 // CU; three or four (one workgroup per CU) measured 1.6-1.8x slower.
 constexpr int PF_STAGES = 2;
+static_assert(PF_STAGES == 2, "the head_dim 128 loop alternates two buffers");
 
 // The work item (query block, head, sequence) of this workgroup; grid
 // (query blocks, heads, sequences).  Workgroup i of a launch runs on XCD
@@ -283,15 +284,36 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
 
   // DMA: instruction i of wave w fills rows 16w + 4i + (lane >> 4), physical
   // chunk lane & 15.  Rows past kv_end read the last needed row (finite; those
-  // keys are masked).  A paged cache: the wave's 16 rows are 16-aligned keys
-  // (or all the clamped last key) inside one block of at least 16 positions,
-  // so the block index is wave-uniform and comes from a scalar load, which
-  // leaves the DMA wait counts alone.
+  // keys are masked).  Contiguous caches: a uniform (scalar) base pointer per
+  // tile plus fixed per-lane offsets, so issuing a tile costs no vector
+  // arithmetic; only the last tile clamps its rows.  A paged cache: the
+  // wave's 16 rows are 16-aligned keys (or all the clamped last key) inside
+  // one block of at least 16 positions, so the block index is wave-uniform
+  // and comes from a scalar load, which leaves the DMA wait counts alone.
   const int rsub = lane >> 4, pch = lane & 15;
   const int vcol = (pch ^ (4 * rsub)) * 8;  // (16w + 4i + rsub) & 3 == rsub
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int koff[4], voff[4];  // element offsets of this lane's rows at key0 = 0
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wave + 4 * i + rsub;
+    koff[i] = r * HD + (pch ^ (r & 15)) * 8;
+    voff[i] = r * HD + vcol;
+  }
+  const size_t head_base = ((size_t)b * a.nkv + j) * a.s_max * HD;
   auto issue = [&](int buf, int key0) {
-    uint8_t* kb = lds + buf * STAGE_B;
+    uint8_t* kb = lds + buf * STAGE_B + 16 * wave_u * ROWB;
     uint8_t* vb = kb + TILE_B;
+    if (!a.pages.table && key0 + PKV <= kv_end) {
+      const ET* ks = kbase + head_base + (size_t)key0 * HD;
+      const ET* vs = vbase + head_base + (size_t)key0 * HD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dma16(ks + koff[i], kb + 4 * i * ROWB);
+        dma16(vs + voff[i], vb + 4 * i * ROWB);
+      }
+      return;
+    }
     size_t base;
     int kmask;
     if (a.pages.table) {
@@ -299,7 +321,7 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
       base = (((size_t)blk * a.nkv + j) << a.pages.log2_bs) * HD;
       kmask = (1 << a.pages.log2_bs) - 1;
     } else {
-      base = ((size_t)b * a.nkv + j) * a.s_max * HD;
+      base = head_base;
       kmask = -1;
     }
 #pragma unroll
@@ -308,8 +330,8 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
       const int key = min(key0 + r, kv_end - 1);
       const int kcol = (pch ^ (r & 15)) * 8;
       const size_t row = base + (size_t)(key & kmask) * HD;
-      dma16(kbase + row + kcol, kb + (16 * wave + 4 * i) * ROWB);
-      dma16(vbase + row + vcol, vb + (16 * wave + 4 * i) * ROWB);
+      dma16(kbase + row + kcol, kb + 4 * i * ROWB);
+      dma16(vbase + row + vcol, vb + 4 * i * ROWB);
     }
   };
 
@@ -321,54 +343,63 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float qk_scale = 1.44269504088896341f / sqrtf((float)HD);
 
-  // Transposed-read addresses (bytes within a V tile) for MFMA (kb, hf, d):
-  // group gi = lane >> 4 covers dims d*32 + (gi & 1)*16 + [0, 16) and keys
-  // kb*32 + hf*16 + (gi >> 1)*4 (+8 for the second read).
-  const int gi = lane >> 4, ii = lane & 15;
-  const int tr_row = (gi >> 1) * 4 + (ii >> 2);            // + kb*32 + hf*16 (+8)
-  const int tr_col = (gi & 1) * 16 + 4 * (ii & 3);         // + d*32
-  // (row & 3) == (ii >> 2) for every read, so the swizzle is fixed per lane.
-  auto tr_off = [&](int row_add, int d) {
-    const int row = tr_row + row_add;
-    const int col = d * 32 + tr_col;
-    return row * ROWB + (((col >> 3) ^ (4 * (ii >> 2))) << 4) + ((col >> 2) & 1) * 8;
-  };
-
-  // Tiles t+1 .. t+PF_STAGES-1 load while tile t is used (8 DMA loads per
-  // wave and tile).
+  // LDS byte offsets of this lane's fragment reads within a tile, fixed for
+  // the whole loop (the buffer, key block and half-tile offsets are
+  // immediates):
+  //  K, MFMA step s: row l32 (+32 kb), chunk (2s + h2) ^ (l32 & 15).
+  //  V transposed reads for dims d*32 + [0, 32): group gi = lane >> 4 covers
+  //  dims (gi & 1)*16 + [0, 16) and keys (gi >> 1)*4 + 4 rows (+ kb*32 +
+  //  hf*16, + 8 for the second read); the swizzle is 4 (row & 3) = 4 e with
+  //  e = ii >> 2 for every read, so chunk (d*4 + c0) ^ 4e = 4 (d ^ e) + c0.
+  int kaddr[HD / 16];
 #pragma unroll
-  for (int t = 0; t < PF_STAGES - 1; ++t)
-    if (t < ntiles) issue(t, t * PKV);
-  for (int tile = 0; tile < ntiles; ++tile) {
+  for (int st = 0; st < HD / 16; ++st) kaddr[st] = l32 * ROWB + (((st * 2 + h2) ^ (l32 & 15)) << 4);
+  const int gi = lane >> 4, ii = lane & 15;
+  const int tr_row = (gi >> 1) * 4 + (ii >> 2);
+  const int tr_col = (gi & 1) * 16 + 4 * (ii & 3);
+  const int e4 = ii >> 2, c0 = tr_col >> 3;
+  int vaddr[HD / 32];
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d)
+    vaddr[d] = TILE_B + tr_row * ROWB + ((4 * (d ^ e4) + c0) << 4) + ((tr_col >> 2) & 1) * 8;
+
+  // Tile t+1 loads while tile t is used (8 DMA loads per wave and tile); the
+  // loop is unrolled by the two buffers so every LDS offset is constant.
+  if (ntiles > 0) issue(0, 0);
+  auto process = [&](auto BUF, int tile) {
+    constexpr int buf = decltype(BUF)::value;
     const int key0 = tile * PKV;
-    const int newer = min(ntiles - 1, tile + PF_STAGES - 2) - tile;
-    if (newer >= 2) wait_vmcnt<16>();
-    else if (newer == 1) wait_vmcnt<8>();
+    if (tile + 1 < ntiles) wait_vmcnt<0>();  // this wave's part of the tile has landed
     else wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();  // tile landed everywhere; tile-1's buffer is free
     __builtin_amdgcn_sched_barrier(0);
-    if (tile + PF_STAGES - 1 < ntiles)
-      issue((tile + PF_STAGES - 1) % PF_STAGES, (tile + PF_STAGES - 1) * PKV);
-    if (key0 > w_last_pos) continue;  // every key of this tile is in this wave's future
-    const uint8_t* kt = lds + (tile % PF_STAGES) * STAGE_B;
-    const uint8_t* vt = kt + TILE_B;
+    if (tile + 1 < ntiles) issue(buf ^ 1, key0 + PKV);
+    if (key0 > w_last_pos) return;  // every key of this tile is in this wave's future
+    const uint8_t* tb = lds + buf * STAGE_B;
 
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+    // K fragments one step ahead of their MFMAs (the scheduler would otherwise
+    // wait for each pair of reads right before its MFMAs).
+    u32x4 kf[2][2];
+    auto kread = [&](int st, int slot) {
+      kf[slot][0] = ld16(tb + kaddr[st]);
+      kf[slot][1] = ld16(tb + kaddr[st] + 32 * ROWB);
+    };
+    kread(0, 0);
+    static_for<0, HD / 16>([&](auto STI) {
+      constexpr int st = decltype(STI)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (st + 1 < HD / 16) kread(st + 1, (st + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < HD / 16; ++s) {
-      const int ch = s * 2 + h2;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kr = kb * 32 + l32;
-        const u32x4 kf = ld16(kt + kr * ROWB + ((ch ^ (kr & 15)) << 4));
-        sacc[kb] = mfma32<DT>(kf, qf[s], sacc[kb]);
-      }
-    }
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32<DT>(kf[st & 1][kb], qf[st], sacc[kb]);
+    });
+    __builtin_amdgcn_sched_barrier(0);
     // Online softmax on unscaled scores; the scale folds into the exponent,
     // p = 2^(s c - m c) with c = log2(e)/sqrt(hd).  The reference max m_run is
     // only raised when a score exceeds it by more than 8 (log2 units), so the
@@ -424,17 +455,21 @@ void attn_prefill_tr_kernel(AttnPrefillArgs a) {
         const u32x4 pb = pack16<DT>(pf);
 #pragma unroll
         for (int d = 0; d < HD / 32; ++d) {
-          const int base = kb * 32 + hf * 16;
+          const int rb = (kb * 32 + hf * 16) * ROWB;
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)(vt + tr_off(base, d)));
+              (__attribute__((address_space(3))) v4i16*)(tb + vaddr[d] + rb));
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)(vt + tr_off(base + 8, d)));
+              (__attribute__((address_space(3))) v4i16*)(tb + vaddr[d] + rb + 8 * ROWB));
           const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2v = __builtin_bit_cast(u32x2, hi);
           const u32x4 va = {l2[0], l2[1], h2v[0], h2v[1]};
           oacc[d] = mfma32<DT>(va, pb, oacc[d]);
         }
       }
     }
+  };
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    process(ic<0>{}, tile);
+    if (tile + 1 < ntiles) process(ic<1>{}, tile + 1);
   }
 
   if (my_t < T) {

@@ -4,6 +4,9 @@ Two summaries, each a short text file that names the command it came from:
 
 * ``stats``: the kernel-trace statistics (calls, average and total duration
   per kernel) of one run.
+* ``counters``: mean per-dispatch values of the SQ/GRBM counters of one
+  kernel over one or more counter runs, with the clock and the MFMA, VALU and
+  LDS mix derived from them.
 * ``traffic``: HBM bytes per launch of one kernel from two counter runs (one
   with FETCH_SIZE, one with WRITE_SIZE).  The counters read in KiB per
   dispatch and do not count every byte the fabric moves, so each is scaled by
@@ -149,6 +152,50 @@ def traffic_summary(fetch_csv: str, write_csv: str, kernel: str, workload: str, 
     return "\n".join(lines) + "\n"
 
 
+def counters_summary(csv_paths: list, kernel: str, workload: str, cmds: list) -> str:
+    """Mean per-dispatch value of every counter collected for `kernel` over
+    one or more counter runs (one file per run), with derived ratios: the
+    shader clock (GRBM_GUI_ACTIVE counts GPU-active cycles summed over the 8
+    XCDs, divided by the dispatch's duration in the same run), MFMA busy per
+    busy CU cycle, and the VALU and LDS instruction mix per MFMA."""
+    pat = re.compile(KERNELS[kernel][0])
+    vals, names, dur = {}, set(), {}
+    for path in csv_paths:
+        means, _, _ = counter_means(path)
+        for (k, c), (v, n) in means.items():
+            if pat.search(k):
+                names.add(k)
+                vals[c] = v
+        ds = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if pat.search(_short(r["Kernel_Name"])):
+                ds[r["Counter_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        for c, v in ds.items():
+            dur[c] = sum(v) / len(v)
+    lines = [f"# Counters of {kernel} ({', '.join(sorted(names))}), workload {workload}", ""]
+    for i, c in enumerate(cmds):
+        lines += [f"Run {i + 1}:", "", "    " + c, ""]
+    lines += [NOTE, "", "| counter | mean per dispatch |", "|---|---:|"]
+    for c in sorted(vals):
+        lines.append(f"| `{c}` | {vals[c]:.4g} |")
+    derived = []
+    if "GRBM_GUI_ACTIVE" in vals and dur.get("GRBM_GUI_ACTIVE"):
+        d = dur["GRBM_GUI_ACTIVE"]
+        derived.append(f"shader clock: {vals['GRBM_GUI_ACTIVE'] / 8 / d / 1e9:.2f} GHz "
+                       f"(GRBM_GUI_ACTIVE / 8 XCDs / {d * 1e6:.1f} us dispatch, profiled)")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "SQ_BUSY_CU_CYCLES" in vals:
+        derived.append(f"MFMA busy per busy CU cycle: {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / vals['SQ_BUSY_CU_CYCLES']:.3f}"
+                       " (SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES)")
+    if "SQ_INSTS_VALU" in vals and "SQ_INSTS_MFMA" in vals:
+        derived.append(f"VALU instructions per MFMA: {vals['SQ_INSTS_VALU'] / max(vals['SQ_INSTS_MFMA'], 1):.2f}")
+    if "SQ_INSTS_LDS" in vals and "SQ_INSTS_MFMA" in vals:
+        derived.append(f"LDS instructions per MFMA: {vals['SQ_INSTS_LDS'] / max(vals['SQ_INSTS_MFMA'], 1):.2f}")
+    if derived:
+        lines += ["", "Derived:", ""] + [f"- {d}" for d in derived]
+    lines += ["", f"sources_sha256: {sources_digest(kernel)}"]
+    return "\n".join(lines) + "\n"
+
+
 def traffic_path(kernel: str, workload: str) -> str:
     return os.path.join(PROFILES, f"{kernel}_{workload}_traffic.md")
 
@@ -186,9 +233,16 @@ def main(argv=None):
     b.add_argument("--copy-mib", type=float, required=True)
     b.add_argument("--cmd-fetch", required=True)
     b.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True, choices=sorted(KERNELS))
+    c.add_argument("--workload", required=True)
+    c.add_argument("--cmd", action="append", required=True)
     args = ap.parse_args(argv)
     if args.cmd_name == "stats":
         sys.stdout.write(format_stats(kernel_stats(args.csv), args.cmd, args.title))
+    elif args.cmd_name == "counters":
+        sys.stdout.write(counters_summary(args.csv, args.kernel, args.workload, args.cmd))
     else:
         sys.stdout.write(traffic_summary(args.fetch_csv, args.write_csv, args.kernel, args.workload,
                                          args.copy_mib, args.cmd_fetch, args.cmd_write))
