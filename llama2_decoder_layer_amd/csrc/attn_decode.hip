@@ -473,6 +473,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnDecodeArgs a) {
   const int nvalid = (pos + a.chunk) / a.chunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t base0 = ((size_t)n * a.nh + h0) * a.nsplit;
+  const int dg = tid % DG, sg = tid / DG;
+  // This thread's first split of every head is loaded before the weights are
+  // computed, so with at most SG splits the partials take one round trip.
+  f32x4 first[GC];
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+    first[h] = sg < nvalid ? *reinterpret_cast<const f32x4*>(
+                                 a.part_acc + ((base0 + (size_t)h * a.nsplit + sg) * HD + dg * 4))
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
   for (int h = wave; h < GC; h += 4) {
     const float* pm = a.part_m + base0 + (size_t)h * a.nsplit;
     const float* pl = a.part_l + base0 + (size_t)h * a.nsplit;
@@ -490,13 +499,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnDecodeArgs a) {
     for (int sp = lane; sp < nvalid; sp += 64) w_s[h * a.nsplit + sp] *= inv;
   }
   __syncthreads();
-  const int dg = tid % DG, sg = tid / DG;
 #pragma unroll
   for (int h = 0; h < GC; ++h) {
     const float* pa = a.part_acc + (base0 + (size_t)h * a.nsplit) * HD + dg * 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (sg < nvalid) acc = w_s[h * a.nsplit + sg] * first[h];
 #pragma unroll 4
-    for (int sp = sg; sp < nvalid; sp += SG)
+    for (int sp = sg + SG; sp < nvalid; sp += SG)
       acc += w_s[h * a.nsplit + sp] * *reinterpret_cast<const f32x4*>(pa + (size_t)sp * HD);
     part[sg][h * DG + dg] = acc;
   }
