@@ -354,14 +354,15 @@ __device__ __forceinline__ void dma_store_tile(const ProjArgs& a,
   }
 }
 
-// Pipeline: k per stage and stages in LDS.  The 256 x 256 tile takes 64-k
-// stages (half the barriers per MFMA of 32-k stages), two of them (128 KB).
+// Pipeline: k per stage and stages in LDS.  The 256 x 256 and 192 x 256
+// tiles take 64-k stages (half the barriers per MFMA of 32-k stages), two of
+// them (128 and 112 KB).
 #ifndef GEMM_BIG_BK
 #define GEMM_BIG_BK 64
 #endif
 template <int BM>
 struct DmaPipe {
-  static constexpr int BK = (BM == 256) ? GEMM_BIG_BK : 32;
+  static constexpr int BK = (BM >= 192) ? GEMM_BIG_BK : 32;
   static constexpr int NST = (BK == 64) ? 2 : 4;
 };
 
@@ -740,11 +741,26 @@ static hipError_t gemm_dma_launch(const ProjArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 192 x 256 tiles (three 32-row blocks per wave) where the 256 x 256 tiles
+// fill more than half of one round, too many to split along K, and the
+// 192-row tiles still fit in one round: the launch then ends after 3/4 of a
+// 256-row tile's work.  The 70B QKV at 1024 tokens (160 tiles of 256 rows,
+// 216 of 192): 206-212 -> 167.5 us, with identical results (each output's sum
+// runs in the same order).  SwiGLU tiles keep 256 rows (gate and up halves).
+static bool dma_mid(int epi, int N, int M, int K) {
+  if (epi == EPI_SWIGLU || K % 64 != 0 || !dma_big(epi, N, M, K)) return false;
+  const long t256 = big_tiles(epi, N, M);
+  const long t192 = (long)((N + 191) / 192) * ((M + 255) / 256);
+  return t256 < GEMM_ROUND && 2 * t256 > GEMM_ROUND && t192 <= GEMM_ROUND;
+}
+
 template <int DT, int EPI, int KVDT>
 static hipError_t gemm_epi(const ProjArgs& a, hipStream_t s) {
-  if (a.K % 32 == 0)
+  if (a.K % 32 == 0) {
+    if (dma_mid(EPI, a.N, a.M, a.K)) return gemm_dma_launch<DT, EPI, 192, 256, KVDT, 8>(a, s);
     return dma_big(EPI, a.N, a.M, a.K) ? gemm_dma_launch<DT, EPI, 256, 256, KVDT, GEMM_BIG_WAVES>(a, s)
                                   : gemm_dma_launch<DT, EPI, 128, 128, KVDT, 4>(a, s);
+  }
   const bool big = use_big_tile(EPI, a.N, a.M);
   return big ? gemm_launch<DT, EPI, 256, 256, KVDT>(a, s) : gemm_launch<DT, EPI, 128, 128, KVDT>(a, s);
 }

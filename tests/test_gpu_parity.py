@@ -208,6 +208,18 @@ def test_bf16_prefill_split_k_tiles():
                      1280, 0, 1280, 131, out_rows=rows)
 
 
+def test_bf16_prefill_192_row_tiles():
+    # 3072 tokens (12 token panels) at hidden 3072, 24 query heads over 2 KV
+    # heads: the QKV (3584 features: 168 tiles of 256 rows, 228 of 192), O and
+    # down (3072: 144 and 192) fill more than half a round of 256 x 256 tiles
+    # and take 192 x 256 tiles; the QKV tile at features 3264-3455 straddles
+    # the k/v boundary (3328).  Rows sampled across token tiles, every K/V
+    # entry checked.
+    rows = np.array([0, 255, 256, 1500, 2047, 2048, 3071])
+    run_prefill_case("bf16-prefill-192", S.Shape(3072, 24, 2, 128, 2048), "bf16", "bf16", 1,
+                     3072, 0, 3072, 141, out_rows=rows)
+
+
 def test_bf16_prefill_wide_f16_cache_mqa():
     run_prefill_case("bf16-prefill-f16kv", S.Shape(256, 4, 1, 64, 512), "bf16", "f16", 1, 130, 3,
                      140, 122)
