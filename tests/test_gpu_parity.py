@@ -127,6 +127,18 @@ def test_f32_hd128_mha():
 # bf16 / f16: token-skinny plan (decode, short prefill)
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("label,shape,act,kv,ctx", [
+    ("piece-bf16", S.Shape(2048, 16, 4, 128, 4096), "bf16", "bf16", [37]),
+    ("piece-f16", S.Shape(2048, 16, 4, 128, 4096), "f16", "f16", [200]),
+    ("piece-k16384", S.Shape(1024, 8, 8, 128, 16384), "bf16", "bf16", [5]),
+])
+def test_decode_one_token_piece_gemv(label, shape, act, kv, ctx):
+    """One token per launch with K a multiple of 2048: O (K = 2048: 8 rows per
+    piece) and down (K = 4096: 4 rows; K = 16384: one row) take the
+    piece-ordered GEMV."""
+    run_decode_case(label, shape, act, kv, ctx, 256, 151)
+
+
 def test_bf16_decode_gqa_f16_cache():
     run_decode_case("bf16-decode-gqa", S.Shape(512, 8, 2, 128, 1376), "bf16", "f16",
                     [0, 1, 63, 64, 65, 300, 511], 512, 110)
