@@ -71,6 +71,52 @@ __device__ __forceinline__ void qkv_epilogue4(const ProjArgs& a, int n, int nl, 
   }
 }
 
+// Two values of runtime format dt at base + idx (idx even).
+__device__ __forceinline__ void store2_rt(void* base, size_t idx, int dt, float a, float b) {
+  if (dt == DT_F32) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(base) + idx) = v;
+  } else {
+    const uint32_t w = dt == DT_BF16 ? pack2<DT_BF16>(a, b) : pack2<DT_F16>(a, b);
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(base) + idx) = w;
+  }
+}
+
+// The QKV epilogue for one RoPE pair: features f, f + 1 (f even).
+template <int DT>
+__device__ __forceinline__ void qkv_epilogue2(const ProjArgs& a, int n, int nl, int f, float* v) {
+  const int b = n / a.T;
+  const int t = n - b * a.T;
+  const int pos = token_position(a, b, t);
+  const int hd = a.hd;
+  const int qdim = a.nh * hd;
+  const int kdim = a.nkv * hd;
+  if (f < qdim + kdim) {
+    const int d = (f < qdim ? f : f - qdim) % hd;
+    const size_t ti = (size_t)pos * (hd >> 1) + (d >> 1);
+    const float c0 = a.rcos[ti], s0 = a.rsin[ti];
+    const float x0 = v[0], y0 = v[1];
+    v[0] = x0 * c0 - y0 * s0;
+    v[1] = x0 * s0 + y0 * c0;
+  }
+  if (f < qdim) {
+    if (a.q32) {
+      store2_rt(a.q32, (size_t)nl * qdim + f, DT_F32, v[0], v[1]);
+    } else {
+      const int h = f / hd, d = f - h * hd;
+      const size_t idx = (((size_t)b * a.nh + h) * a.T + t) * hd + d;
+      store2_rt(a.q16, idx, a.kv_dt, v[0], v[1]);
+    }
+  } else if (f < qdim + kdim) {
+    const int j = (f - qdim) / hd, d = (f - qdim) - j * hd;
+    store2_rt(a.kc, kv_row(a.pages, b, j, pos, a.nkv, a.s_max, hd) + d, a.kv_dt, v[0], v[1]);
+  } else {
+    const int j = (f - qdim - kdim) / hd, d = (f - qdim - kdim) - j * hd;
+    store2_rt(a.vc, kv_row(a.pages, b, j, pos, a.nkv, a.s_max, hd) + d, a.kv_dt, v[0], v[1]);
+  }
+}
+
 // Weight row pointer for output feature f of a segmented projection.
 template <typename T>
 __device__ __forceinline__ const T* seg_row(const ProjArgs& a, int f) {
