@@ -129,6 +129,19 @@ def test_paged_gqa8_whole_contexts():
                    152)
 
 
+@pytest.mark.parametrize("label,shape,kv", [
+    ("paged-piece-4", S.Shape(2048, 16, 4, 128, 4096), "bf16"),
+    ("paged-piece-4-f16", S.Shape(2048, 16, 4, 128, 4096), "f16"),
+    ("paged-piece-2", S.Shape(8192, 64, 8, 128, 1024), "bf16"),
+])
+def test_paged_one_token_piece_gemv(label, shape, kv):
+    """One sequence (one token per launch) with hidden 2048 or 8192: the QKV
+    projection runs the piece-ordered kernel, whose epilogue (groups of 4
+    features, or RoPE pairs at K = 8192) writes K and V through the block
+    table; the new position opens a block."""
+    run_paged_case(label, shape, "bf16", kv, [64], 128, 16, 157, oracle=True)
+
+
 def test_paged_f32_cache_single_block():
     run_paged_case("paged-f32", S.TINY, "f32", "f32", [3, 20, 23], 24, 256, 153, oracle=True)
 
