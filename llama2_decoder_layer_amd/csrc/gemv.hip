@@ -12,8 +12,8 @@
 //
 // Four variants:
 //  * gemv_row1 (1-4 tokens): each wave streams one row over the full K; see below.
-//  * gemv_piece (one token, residual epilogue, K a multiple of 2048): workgroups
-//    walk the matrix in 32 KB pieces of whole rows; see below.
+//  * gemv_piece (one token, K a multiple of 2048: O, down, and QKV with its
+//    norm): workgroups walk the matrix in 32 KB pieces of whole rows; see below.
 //  * gemv_lds: the activations of the M tokens (M*K*size <= 48 KB) are staged
 //    once per workgroup in LDS.  With a fused RMSNorm the staging pass also
 //    multiplies by the gain and accumulates sum x^2, so 1/rms is known before
@@ -766,16 +766,18 @@ hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// One token, residual epilogue, no norm, K a multiple of 2048 (16-bit formats):
-// workgroups walk the weight matrix in pieces of R whole rows (R K 2 bytes =
-// 32 KB, or one longer row) with a grid-stride loop, the next piece's loads
-// in flight during the current piece's products.  The requests in flight then
-// cover a compact stretch of memory, where one row per wave has every row of
-// the matrix open at once: a copy of the row kernel stripped of its
-// activation stage, products and epilogue ran no faster than the whole
-// kernel (70B O 27.0 against 27.4 us, against 23.5 for a plain read), so the
-// access pattern is the difference.  70B O 27.4 -> 25.4 us, down (one 56 KB
-// row per piece) 75.7 -> 74.0 us over cold weight copies.
+// One token, 16-bit formats, K a multiple of 2048: the residual projections
+// (O, down) and the QKV projection with its fused norm.  Workgroups walk the
+// weight matrix in pieces of R whole rows (R K 2 bytes = 32 KB, or one longer
+// row) with a grid-stride loop, the next piece's loads in flight during the
+// current piece's products.  The requests in flight then cover a compact
+// stretch of memory, where one row per wave has every row of the matrix open
+// at once: a copy of the row kernel stripped of its activation stage,
+// products and epilogue ran no faster than the whole kernel (70B O 27.0
+// against 27.4 us, against 23.5 for a plain read), so the access pattern is
+// the difference.  70B O 27.4 -> 25.4 us, down (one 56 KB row per piece)
+// 75.7 -> 74.0 us over cold weight copies; QKV 31.4 -> 30.2 us in the
+// 80-layer stack.
 // Thread t takes chunks t + 256 i of a piece: chunk i is in row i / KCB at
 // k = 8 (t + 256 (i % KCB)), so each thread's KCB activation chunks serve
 // every row of every piece and stay in registers; the row sums meet in LDS.
