@@ -393,15 +393,19 @@ def bench_sample(args, wl):
         B.llama_sample(logits, hist, u, ids, e["temperature"], e["top_k"], e["top_p"], e["penalty"])
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    kid = B.kernel_id("sample")
-    B.llama_layer_timer_start(kid, args.steps)
+    # Timed loop without events, then the same calls with the kernel's own
+    # events (the roofline), as for the layer workloads.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    kid = B.kernel_id("sample")
+    B.llama_layer_timer_start(kid, args.steps)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     kms, kn = B.llama_layer_timer_stop()
     ms_step = el * 1e3 / args.steps
     kavg_s = kms / 1e3 / max(kn, 1)
