@@ -168,11 +168,12 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
     src[j] = row + k0;
     kofs[j] = c * 8;
   }
-  // Workgroup blk walks the stages of its K range starting at stage blk mod
-  // nkt and wraps around (only when the range is whole stages).  Otherwise
-  // every resident workgroup reads the same 512-byte slot of its 16 KB rows at
-  // the same moment: 70B gate/up at 32 tokens 167.6 -> 151.5 us.
-  const int rot = (klen % BK == 0) ? blk % nkt : 0;
+  // Without a K split, workgroup blk walks the stages of K starting at stage
+  // blk mod nkt and wraps around (when K is whole stages).  Otherwise every
+  // resident workgroup reads the same 512-byte slot of its 16 KB rows at the
+  // same moment: 70B gate/up at 32 tokens 167.6 -> 151.5 us.  Split launches
+  // already put neighbouring workgroups on different K ranges.
+  const int rot = (nsplit == 1 && klen % BK == 0) ? blk % nkt : 0;
   auto issue = [&](int st, int kt) {
     uint8_t* base = lds + st * G::STAGE;
     const int kr = kt + rot < nkt ? kt + rot : kt + rot - nkt;
@@ -399,8 +400,8 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
       esz[j] = 2;
     }
   }
-  // Stages in rotated order, as in the 16-bit kernel.
-  const int rot = (klen % W8_BK == 0) ? blk % nkt : 0;
+  // Stages in rotated order without a K split, as in the 16-bit kernel.
+  const int rot = (nsplit == 1 && klen % W8_BK == 0) ? blk % nkt : 0;
   auto issue = [&](int st, int kt) {
     uint8_t* base = lds + st * G::STAGE;
     const int kr = kt + rot < nkt ? kt + rot : kt + rot - nkt;
