@@ -66,10 +66,51 @@ static int w8_features(int epi) { return epi == EPI_SWIGLU ? W8_BMW / 2 : W8_BMW
 // Weight rows of a launch: N (SwiGLU: gate rows then up rows, 2N).
 static int sk_rows(int epi, int N) { return epi == EPI_SWIGLU ? 2 * N : N; }
 
-// Epilogue for four consecutive features f..f+3 of token m.
+// Deferred norm: each token has SK_SSQ_MAX partial-sum slots in a.ssq (16
+// floats, 64 bytes); slots past a.ssq_parts hold zeros, so readers sum all of
+// them in slot order (hidden sizes up to 16384).
+constexpr int SK_SSQ_MAX = 16;
+
+// 1 / rms of token m's input from the partial sums of squares that the
+// residual projection before it left in a.ssq.
+__device__ __forceinline__ float sk_rstd(const ProjArgs& a, int m) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(a.ssq + (size_t)m * SK_SSQ_MAX);
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < SK_SSQ_MAX / 4; ++i) {
+    const f32x4 v = p[i];
+    t += v[0]; t += v[1]; t += v[2]; t += v[3];
+  }
+  return 1.0f / sqrtf(t / (float)a.K + a.eps);
+}
+
+// A lane's slots for sk_rstd, loaded ahead (after a k loop's first loads are
+// issued) so that their latency is not paid at the end of the workgroup.
+struct SsqAhead {
+  f32x4 v[SK_SSQ_MAX / 4];
+  __device__ __forceinline__ void load(const ProjArgs& a, int m) {
+    if (!a.ssq) return;
+    const f32x4* p = reinterpret_cast<const f32x4*>(a.ssq + (size_t)(m < a.M ? m : 0) * SK_SSQ_MAX);
+#pragma unroll
+    for (int i = 0; i < SK_SSQ_MAX / 4; ++i) v[i] = p[i];
+  }
+  // Summed in the order sk_rstd uses.
+  __device__ __forceinline__ float rstd(const ProjArgs& a) const {
+    if (!a.ssq) return 1.0f;
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < SK_SSQ_MAX / 4; ++i) {
+      t += v[i][0]; t += v[i][1]; t += v[i][2]; t += v[i][3];
+    }
+    return 1.0f / sqrtf(t / (float)a.K + a.eps);
+  }
+};
+
+// Epilogue for four consecutive features f..f+3 of token m.  SwiGLU: r is
+// the deferred norm's 1/rms of the token (1 without one).
 template <int DT, int EPI>
 __device__ __forceinline__ void sk_store4(const ProjArgs& a, int m, int f, const float* v,
-                                          const float* up) {
+                                          const float* up, float r = 1.0f) {
   typedef typename Elt<DT>::T T;
   if constexpr (EPI == EPI_LOGITS) {
     float* y = reinterpret_cast<float*>(a.y) + (size_t)m * a.N;
@@ -84,8 +125,8 @@ __device__ __forceinline__ void sk_store4(const ProjArgs& a, int m, int f, const
     store4<DT>(y, rv[0] + v[0], rv[1] + v[1], rv[2] + v[2], rv[3] + v[3]);
   } else if constexpr (EPI == EPI_SWIGLU) {
     T* y = reinterpret_cast<T*>(a.y) + (size_t)m * a.N + f;
-    store4<DT>(y, silu(v[0]) * up[0], silu(v[1]) * up[1], silu(v[2]) * up[2],
-               silu(v[3]) * up[3]);
+    store4<DT>(y, silu(r * v[0]) * (r * up[0]), silu(r * v[1]) * (r * up[1]),
+               silu(r * v[2]) * (r * up[2]), silu(r * v[3]) * (r * up[3]));
   } else {
     float w[4] = {v[0], v[1], v[2], v[3]};
     qkv_epilogue4<DT>(a, a.tok0 + m, m, f, w);
@@ -206,10 +247,11 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
     if (st < nkt) issue(st, st);
+  SsqAhead ssq;  // deferred norm of a SwiGLU launch without a K split
+  if constexpr (SWI && !SPLIT) ssq.load(a, l32);
   // The barrier is a bare s_barrier: a full __syncthreads would also wait for
   // the stages still in flight.  Its explicit waits: this wave's loads of stage
   // kt (vmcnt) and its reads of stage kt-1, which the MFMAs consumed.  The
@@ -275,6 +317,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   } else if constexpr (SWI) {
     if (m >= a.M) return;
     const f32x16 up = red[lane];
+    const float r = ssq.rstd(a);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int f = f0 + g * 8 + h2 * 4;
@@ -282,7 +325,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
       float v[4], u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[i] = acc[g * 4 + i]; u[i] = up[g * 4 + i]; }
-      sk_store4<DT, EPI>(a, m, f, v, u);
+      sk_store4<DT, EPI>(a, m, f, v, u, r);
     }
   } else {
     if (m >= a.M) return;
@@ -440,10 +483,11 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-
 #pragma unroll
   for (int st = 0; st < G::NST - 1; ++st)
     if (st < nkt) issue(st, st);
+  SsqAhead ssq;  // deferred norm of a SwiGLU launch without a K split
+  if constexpr (SWI && !SPLIT) ssq.load(a, l32);
   for (int kt = 0; kt < nkt; ++kt) {
     wait_stage(min(nkt - 1, kt + G::NST - 2) - kt);
     __builtin_amdgcn_sched_barrier(0);
@@ -517,6 +561,7 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
   } else if constexpr (SWI) {
     if (m >= a.M) return;
     const f32x16 up = red[rb * 64 + lane];
+    const float r = ssq.rstd(a);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int f = f0 + rb * 32 + g * 8 + h2 * 4;
@@ -524,7 +569,7 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
       float v[4], u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[i] = acc[g * 4 + i]; u[i] = up[g * 4 + i]; }
-      sk_store4<DT, EPI>(a, m, f, v, u);
+      sk_store4<DT, EPI>(a, m, f, v, u, r);
     }
   } else {
     if (m >= a.M) return;
@@ -541,9 +586,13 @@ __global__ __launch_bounds__(W8_NW * 64) void gemv_dma_w8_kernel(ProjArgs a, flo
 }
 
 // Sum of the K-split partials and the epilogue; one thread per (token, 4 features).
+// With a.nout (EPI_RESID, N % 1024 == 0, so a workgroup is 1024 features of
+// one token): y as stored, y * ngamma into nout, and the workgroup's sum of
+// the stored y^2 into its slot of a.ssq.
 template <int DT, int EPI>
 __global__ __launch_bounds__(256) void gemv_split_reduce_kernel(ProjArgs a, const float* part,
                                                                 int nsplit) {
+  typedef typename Elt<DT>::T T;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   const int nf4 = (a.N + 3) / 4;
   const int id = blockIdx.x * 256 + threadIdx.x;
@@ -557,6 +606,38 @@ __global__ __launch_bounds__(256) void gemv_split_reduce_kernel(ProjArgs a, cons
     if constexpr (SWI) u += *reinterpret_cast<const f32x4*>(p + a.N + f);
   }
   float vv[4] = {v[0], v[1], v[2], v[3]}, uu[4] = {u[0], u[1], u[2], u[3]};
+  if constexpr (SWI) {
+    sk_store4<DT, EPI>(a, m, f, vv, uu, a.ssq ? sk_rstd(a, m) : 1.0f);
+    return;
+  }
+  if constexpr (EPI == EPI_RESID) {
+    if (a.nout) {
+      float rv[4], yv[4], gv[4];
+      load4<DT>(reinterpret_cast<const T*>(a.resid) + (size_t)m * a.N + f, rv);
+      const u32x2 yp = {pack2<DT>(rv[0] + vv[0], rv[1] + vv[1]),
+                        pack2<DT>(rv[2] + vv[2], rv[3] + vv[3])};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.y) + (size_t)m * a.N + f) = yp;
+      // The stored values: what a norm pass would read.
+      yv[0] = Elt<DT>::to_f32(yp[0] & 0xffffu);
+      yv[1] = Elt<DT>::to_f32(yp[0] >> 16);
+      yv[2] = Elt<DT>::to_f32(yp[1] & 0xffffu);
+      yv[3] = Elt<DT>::to_f32(yp[1] >> 16);
+      load4<DT>(reinterpret_cast<const T*>(a.ngamma) + f, gv);
+      store4<DT>(reinterpret_cast<T*>(a.nout) + (size_t)m * a.N + f, yv[0] * gv[0],
+                 yv[1] * gv[1], yv[2] * gv[2], yv[3] * gv[3]);
+      float ss = yv[0] * yv[0] + yv[1] * yv[1] + yv[2] * yv[2] + yv[3] * yv[3];
+      ss = wave_sum(ss);
+      __shared__ float wsum[4];
+      if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+      __syncthreads();
+      float* slots = a.ssq + (size_t)m * SK_SSQ_MAX;
+      if (threadIdx.x == 0) slots[f >> 10] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      // The token's first workgroup zeroes the unused slots.
+      if (f < 1024 && threadIdx.x >= a.ssq_parts && threadIdx.x < SK_SSQ_MAX)
+        slots[threadIdx.x] = 0.f;
+      return;
+    }
+  }
   sk_store4<DT, EPI>(a, m, f, vv, uu);
 }
 
@@ -571,6 +652,15 @@ size_t gemv_dma_partial_floats(int epi, int N, int K, int M) {
 
 bool gemv_dma_supported(int dt, int M, int K, int N) {
   return dt != DT_F32 && M >= 1 && M <= SK_BN && K % 64 == 0 && N % 4 == 0;
+}
+
+int gemv_dma_norm_parts(int dt, bool w8, int M, int N_o, int K_o, int I) {
+  if (dt != DT_BF16 || M <= 4 || N_o % 1024 != 0 || N_o / 1024 > SK_SSQ_MAX) return 0;
+  if (!gemv_dma_supported(dt, M, K_o, N_o) || !gemv_dma_supported(dt, M, N_o, I)) return 0;
+  int kchunk;
+  const int ns = w8 ? sk_split_f(w8_features(EPI_RESID), N_o, K_o, &kchunk, W8_TARGET_WG)
+                    : sk_split(EPI_RESID, N_o, K_o, &kchunk);
+  return ns > 1 ? N_o / 1024 : 0;
 }
 
 template <int DT, int EPI, int BK, int NST>

@@ -68,6 +68,17 @@ struct ProjArgs {
   const float* wscale[3];  // int8 / int4 weights: float32 scale per row of each segment
   int wbits;               // quantised weights: 8 (int8 codes) or 4 (packed int4 codes)
   KvPages pages;           // paged caches (pages.table == nullptr: contiguous)
+  // RMSNorm of the next projection's input, deferred into the streaming
+  // kernels (bf16 activations).  An EPI_RESID K-split launch with nout set
+  // also writes nout = y * ngamma [M, N] and, for token m, the sum of y^2 over
+  // features 1024 g .. 1024 g + 1023 into ssq[16 m + g] (g < ssq_parts =
+  // N / 1024 <= 16; the other slots of the 16 get zeros).  An EPI_SWIGLU
+  // launch with ssq set multiplies both of its sums by
+  // 1 / sqrt(sum of the 16 slots / K + eps) before the SwiGLU.
+  void* nout;
+  const void* ngamma;
+  float* ssq;
+  int ssq_parts;
 };
 
 // Decode-sized projection (M <= 32 tokens).  A fused norm (gamma != nullptr)
@@ -85,6 +96,11 @@ hipError_t launch_gemv_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
 // Weight-only int8 through the LDS-streaming kernel (16-bit activations, M <= 32,
 // K % 64 == 0, no fused norm; partials as gemv_dma_partial_floats).
 hipError_t launch_gemv_dma_w8(int dt, int epi, const ProjArgs& a, hipStream_t s);
+// Partial sums per token (N_o / 1024) with which the residual projection
+// [N_o x K_o] at M tokens can defer the norm of its output into the gate/up
+// projection [2 I x N_o] (int8 weights when w8), or 0 when the two launches
+// do not take the streaming paths that implement it.
+int gemv_dma_norm_parts(int dt, bool w8, int M, int N_o, int K_o, int I);
 // Positions [start, start + count) of every (sequence, KV head) of contiguous
 // caches [B, nkv, s_max, hd] copied into the pools of a paged cache.
 hipError_t launch_kv_pages_write(const void* k_src, const void* v_src, int s_max, int start,

@@ -122,7 +122,7 @@ static bool wide_plan(const ll_config* c, int64_t tokens_total, bool decode) {
 }
 
 struct Layout {
-  size_t q32, pm, pl, pacc, part, u, q16, o, h1, a, total;
+  size_t q32, pm, pl, pacc, part, ssq, u, q16, o, h1, a, total;
   int nsplit_max;
 };
 
@@ -166,6 +166,8 @@ static Layout layout(const ll_config* c, int64_t bt, int s_max, bool wide, int n
       pf = std::max(pf, gemv_dma_partial_floats(EPI_RESID, H, I, m));
     }
     L.part = take(pf * 4);
+    // Partial sums of squares of a deferred FFN norm: 16 slots per token.
+    L.ssq = take(g * 16 * 4);
   }
   L.o = take(bt * qd * act);
   L.h1 = take(bt * c->hidden * act);
@@ -227,6 +229,13 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
   };
 
   float* part = (float*)(ws + L.part);
+  // Without a fused norm, the FFN norm can ride on the O projection's K-split
+  // reduction (h1 * gamma and partial sums of squares) and the gate/up
+  // epilogue (the 1/rms factor), which saves the norm pass: 'deferred' is
+  // the number of partial sums per token, or 0.
+  const int deferred =
+      fuse_norm || wbits == 4 ? 0 : gemv_dma_norm_parts(dt, w8 != nullptr, m, H, qd, I);
+  float* ssq = (float*)(ws + L.ssq);
 
   // 1. QKV + RMSNorm + RoPE + cache append.
   ProjArgs p = base_args(c);
@@ -304,12 +313,17 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
   po.w[0] = w8 ? (const void*)w8->w_o : w->w_o; po.seg1 = po.seg2 = H;
   if (w8) po.wscale[0] = w8->s_o;
   po.N = H; po.K = qd; po.M = m; po.x = o; po.resid = xm; po.y = h1;
+  if (deferred) {
+    po.nout = u; po.ngamma = ffn_norm; po.ssq = ssq; po.ssq_parts = deferred;
+  }
   timer_before(KID_GEMV_O, s);
   LL_TRY(proj(EPI_RESID, po));
   timer_after(KID_GEMV_O, s);
 
   // 4. gate/up + RMSNorm + SwiGLU.
   ProjArgs pg = base_args(c);
+  pg.ssq = deferred ? ssq : nullptr;
+  pg.ssq_parts = deferred;
   pg.part = part;
   if (w8) {
     pg.w[0] = w8->w_gate; pg.w[1] = w8->w_up;
@@ -320,6 +334,8 @@ static int run_skinny(const ll_config* c, const ll_weights* w, const ll_weights_
   pg.N = I; pg.K = H; pg.M = m; pg.y = a;
   if (fuse_norm) {
     pg.x = h1; pg.gamma = ffn_norm;
+  } else if (deferred) {
+    pg.x = u;  // h1 * gamma from the O projection's reduction
   } else {
     timer_before(KID_RMSNORM, s);
     LL_TRY(launch_rmsnorm(dt, h1, ffn_norm, u, m, H, c->eps, s));

@@ -12,6 +12,7 @@ import torch
 
 from gpu_util import (TOL, DeviceLayer, check_errors, delta_error, from_dev, oracle_cfg,
                       oracle_weights, random_layer, rel_err, scale_stored, to_dev)
+from llama2_decoder_layer_amd import binding as B
 from llama2_decoder_layer_amd import synth as S
 from oracle import llama_ref as R
 
@@ -155,6 +156,27 @@ def test_bf16_decode_gqa8_hd64_long():
 def test_bf16_decode_batch_over_32():
     ctx = list(np.random.Generator(np.random.PCG64(5)).integers(0, 200, 40))
     run_decode_case("bf16-decode-b40", S.Shape(256, 4, 1, 64, 688), "bf16", "bf16", ctx, 256, 111)
+
+
+@pytest.mark.parametrize("label,act,x_scale,norm_passes", [
+    ("deferred-ffn-norm", "bf16", 1.0, 1),
+    ("deferred-ffn-norm-small-x", "bf16", 2.0 ** -8, 1),
+    ("f16-ffn-norm-pass", "f16", 1.0, 2),
+])
+def test_decode_deferred_ffn_norm(label, act, x_scale, norm_passes):
+    """24 tokens at hidden 2048 with learned gains: the O projection takes the
+    K-split streaming path, so with bf16 activations its reduction also writes
+    h1 * ffn_norm and per-token partial sums of h1^2, and the gate/up epilogue
+    applies 1/rms; one norm pass per call instead of two.  f16 activations keep
+    the pass.  The small-x case makes the branches dominate the output."""
+    ctx = list(np.random.Generator(np.random.PCG64(9)).integers(0, 500, 24))
+    B.llama_layer_timer_start(B.kernel_id("rmsnorm"), 16)
+    try:
+        run_decode_case(label, S.Shape(2048, 16, 4, 128, 5632), act, "f16", ctx, 512, 160,
+                        x_scale=x_scale)
+    finally:
+        _, launches = B.llama_layer_timer_stop()
+    assert launches == norm_passes, (label, launches)
 
 
 def test_f16_decode_mha():
