@@ -6,8 +6,10 @@
 // one K range.  Weights and activations move global -> LDS by
 // global_load_lds in 256-k stages (512-byte row slices), three deep (144 KB of
 // LDS, one workgroup per CU), so each row has 1 KB in flight and each CU
-// 64 KB of weights.  The four waves split a stage's work as 2 row blocks x 2
-// k halves of v_mfma_f32_32x32x16; the k halves meet in LDS at the end.
+// 64 KB of weights.  The eight waves split a stage's work as 2 row blocks x 4
+// k slices of v_mfma_f32_32x32x16; the k slices meet in LDS at the end (four
+// waves with k halves: 70B gate/up at 32 tokens 155.5 -> 154.0 us, step
+// 380.5 -> 377.3 us).
 // Measured on the 70B gate/up at 32 tokens against 64-k stages four deep with
 // three workgroups per CU (128-byte slices, 384 bytes per row in flight):
 // 183 -> 173 us; 128-k stages six deep (one workgroup per CU) were slower
@@ -30,6 +32,7 @@ constexpr int SK_BM = 64;                          // weight rows per workgroup
 constexpr int SK_BN = 32;                          // token slots
 constexpr int SK_BK = 256;                         // k per stage
 constexpr int SK_NST = 3;                          // stages in LDS
+constexpr int SK_NW = 8;                           // waves per workgroup
 constexpr int SK_TARGET_WG = 512;                  // workgroups wanted per launch
 constexpr int SK_MAX_SPLIT = 8;
 
@@ -139,17 +142,19 @@ __device__ __forceinline__ void sk_store4(const ProjArgs& a, int m, int f, const
 // NIW per wave.  Chunk c of row r sits at physical chunk c ^ (r & 15): the 16
 // rows that one ds_read_b128 cycle serves then land in 16 distinct 4-bank
 // groups.
-template <int BK, int NST>
+template <int BK, int NST, int NW>
 struct SkGeom {
   static_assert(BK == 64 || BK == 128 || BK == 256, "stage width");
+  static_assert(NW == 4 || NW == 8, "waves");
   static constexpr int ROWB = BK * 2;
   static constexpr int CPR = ROWB / 16;
   static constexpr int RPI = 64 / CPR;
   static constexpr int NI = (SK_BM + SK_BN) / RPI;
-  static constexpr int NIW = NI / 4;
-  static constexpr int NIW_W = (SK_BM / RPI) / 4;  // weight instructions per wave
+  static constexpr int NIW = NI / NW;
+  static constexpr int NIW_W = (SK_BM / RPI) / NW;  // weight instructions per wave
   static constexpr int STAGE = (SK_BM + SK_BN) * ROWB;
-  static constexpr int KS2 = BK / 32;              // 32x32x16 k-steps per wave per stage
+  static constexpr int KSL = NW / 2;               // k slices of a stage (2 row blocks)
+  static constexpr int KS2 = BK / 16 / KSL;        // 32x32x16 k-steps per wave per stage
   static constexpr int LDS = NST * STAGE;
   static_assert(NIW * (NST - 2) < 64, "vmcnt range");
   // Physical chunk = logical chunk ^ swz(row).  128-byte slices put two rows
@@ -158,16 +163,17 @@ struct SkGeom {
 };
 
 template <int DT, int EPI, bool SPLIT, int BK, int NST>
-__global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, int kchunk, int nsplit) {
+__global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float* part, int kchunk,
+                                                              int nsplit) {
   typedef typename Elt<DT>::T T;
-  typedef SkGeom<BK, NST> G;
+  typedef SkGeom<BK, NST, SK_NW> G;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
   constexpr int FB = SWI ? SK_BM / 2 : SK_BM;  // features per workgroup
   // One LDS object: the stage ring, reused at the end for the cross-wave sums.
   // (A second LDS variable gives the accesses alias scopes, and the wait-count
   // pass then waits for every outstanding DMA before each fragment read.)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS];
-  f32x16* red = reinterpret_cast<f32x16*>(lds);  // [2][64] after the k loop
+  f32x16* red = reinterpret_cast<f32x16*>(lds);  // [KSL - 1][2][64] after the k loop
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = a.K;
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   const int nkt = (klen + BK - 1) / BK;
 
   // DMA: instruction i of a stage fills stage rows RPI*i .. RPI*i + RPI-1
-  // (rows 0..63 weights, 64..95 token slots); wave w issues i = w + 4j.  Lane
+  // (rows 0..63 weights, 64..95 token slots); wave w issues i = w + NW j.  Lane
   // l: row RPI*i + l/CPR, physical chunk l%CPR, logical chunk phys ^ (row&15).
   // A chunk past the end of the K range (last stage of a range that is not a
   // multiple of BK) re-reads the range's first chunk instead; the k-steps that
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   int kofs[G::NIW];
 #pragma unroll
   for (int j = 0; j < G::NIW; ++j) {
-    const int i = wave + 4 * j;
+    const int i = wave + SK_NW * j;
     const int r = G::RPI * i + lane / G::CPR;
     const int c = (lane % G::CPR) ^ G::swz(r);
     const T* row;
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
     for (int j = 0; j < G::NIW; ++j) {
       const int kk = k + kofs[j];
       const T* g = src[j] + (kk < klen ? kk : 0);
-      uint8_t* d = base + (wave + 4 * j) * 1024;
+      uint8_t* d = base + (wave + SK_NW * j) * 1024;
       if (j < G::NIW_W) dma16_stream(g, d);  // weights: instructions 0 .. 64/RPI - 1
       else dma16(g, d);                      // activations
     }
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
   };
 
   // Fragments: wave w multiplies row block rb = w & 1 over the k-steps
-  // kh*KS2 .. kh*KS2 + KS2-1 (kh = w >> 1) of every stage.
+  // kh*KS2 .. kh*KS2 + KS2-1 (k slice kh = w >> 1) of every stage.
   const int rb = wave & 1, kh = wave >> 1;
   const int l32 = lane & 31, h2 = lane >> 5;
   const int swz = G::swz(l32);  // rows rb*32 + l32 and token row 64 + l32 share it
@@ -283,12 +289,15 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // k halves meet: waves 2, 3 hand their sums to waves 0, 1 (once every wave
+  // k slices meet: waves 2.. hand their sums to waves 0, 1 (once every wave
   // is done with the last stage, whose buffer may be the one reused).
   __syncthreads();
-  if (kh == 1) red[rb * 64 + lane] = acc;
+  if (kh > 0) red[((kh - 1) * 2 + rb) * 64 + lane] = acc;
   __syncthreads();
-  if (kh == 0) acc += red[rb * 64 + lane];
+  if (kh == 0) {
+#pragma unroll
+    for (int q = 0; q < G::KSL - 1; ++q) acc += red[(q * 2 + rb) * 64 + lane];
+  }
   if constexpr (!SPLIT && SWI) {
     // Gate rows are in wave 0, the matching up rows in wave 1.
     __syncthreads();
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(ProjArgs a, float* part, 
     __syncthreads();
     if (wave != 0) return;
   }
-  if (kh == 1) return;
+  if (kh > 0) return;
 
   // Lane holds token l32 and rows rb*32 + g*8 + h2*4 + 0..3, g = 0..3.
   const int m = l32;
@@ -669,12 +678,12 @@ static hipError_t gemv_dma_cfg(const ProjArgs& a, hipStream_t s) {
   const int ns = sk_split(EPI, a.N, a.K, &kchunk);
   const int nblk = (a.N + sk_features(EPI) - 1) / sk_features(EPI);
   if (ns == 1) {
-    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false, BK, NST>), dim3(nblk), dim3(256), 0, s, a,
+    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false, BK, NST>), dim3(nblk), dim3(SK_NW * 64), 0, s, a,
               (float*)nullptr, kchunk, 1);
     return hipGetLastError();
   }
   if (!a.part) return hipErrorInvalidValue;
-  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true, BK, NST>), dim3(nblk * ns), dim3(256), 0, s, a, a.part,
+  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true, BK, NST>), dim3(nblk * ns), dim3(SK_NW * 64), 0, s, a, a.part,
             kchunk, ns);
   const int n = ((a.N + 3) / 4) * a.M;
   LL_LAUNCH((gemv_split_reduce_kernel<DT, EPI>), dim3((n + 255) / 256), dim3(256), 0, s, a,
