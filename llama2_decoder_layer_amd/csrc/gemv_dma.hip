@@ -28,16 +28,24 @@
 
 namespace ll {
 
+// Two workgroup shapes: 64 weight rows in 256-k stages three deep (144 KB of
+// LDS), and 128 rows in 128-k stages four deep (160 KB, 96 KB of weights in
+// flight per CU).  The 128-row shape serves launches that need no K split
+// (70B gate/up at 32 tokens: 153.0 -> 141.8 us); K-split launches keep 64
+// rows (O, down and QKV were each ~1 us slower with 128).
 constexpr int SK_BM = 64;                          // weight rows per workgroup
-constexpr int SK_BN = 32;                          // token slots
 constexpr int SK_BK = 256;                         // k per stage
 constexpr int SK_NST = 3;                          // stages in LDS
+constexpr int SK_BM_W = 128;                       // the same, 128-row shape
+constexpr int SK_BK_W = 128;
+constexpr int SK_NST_W = 4;
+constexpr int SK_BN = 32;                          // token slots
 constexpr int SK_NW = 8;                           // waves per workgroup
 constexpr int SK_TARGET_WG = 512;                  // workgroups wanted per launch
 constexpr int SK_MAX_SPLIT = 8;
 
-// Features covered by one workgroup and the number of K splits used.
-static int sk_features(int epi) { return epi == EPI_SWIGLU ? SK_BM / 2 : SK_BM; }
+// Features covered by one workgroup of bm rows.
+static int sk_features(int epi, int bm = SK_BM) { return epi == EPI_SWIGLU ? bm / 2 : bm; }
 
 // Splits of K for a launch whose workgroups cover `feats` features each, to
 // reach about `target` workgroups.
@@ -56,8 +64,14 @@ static int sk_split_f(int feats, int N, int K, int* kchunk, int target = SK_TARG
   return (nkt + kt_per - 1) / kt_per;
 }
 
-static int sk_split(int epi, int N, int K, int* kchunk) {
-  return sk_split_f(sk_features(epi), N, K, kchunk);
+static int sk_split(int epi, int N, int K, int* kchunk, int bm = SK_BM) {
+  return sk_split_f(sk_features(epi, bm), N, K, kchunk);
+}
+
+// Whether a launch takes the 128-row shape: when it needs no K split there.
+static bool sk_wide(int epi, int N, int K) {
+  int kchunk;
+  return sk_split(epi, N, K, &kchunk, SK_BM_W) == 1;
 }
 
 // Code rows per workgroup of the int8 streaming kernel, its features, and the
@@ -142,19 +156,21 @@ __device__ __forceinline__ void sk_store4(const ProjArgs& a, int m, int f, const
 // NIW per wave.  Chunk c of row r sits at physical chunk c ^ (r & 15): the 16
 // rows that one ds_read_b128 cycle serves then land in 16 distinct 4-bank
 // groups.
-template <int BK, int NST, int NW>
+template <int BK, int NST, int NW, int BM>
 struct SkGeom {
   static_assert(BK == 64 || BK == 128 || BK == 256, "stage width");
   static_assert(NW == 4 || NW == 8, "waves");
   static constexpr int ROWB = BK * 2;
   static constexpr int CPR = ROWB / 16;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int NI = (SK_BM + SK_BN) / RPI;
+  static constexpr int NI = (BM + SK_BN) / RPI;
   static constexpr int NIW = NI / NW;
-  static constexpr int NIW_W = (SK_BM / RPI) / NW;  // weight instructions per wave
-  static constexpr int STAGE = (SK_BM + SK_BN) * ROWB;
-  static constexpr int KSL = NW / 2;               // k slices of a stage (2 row blocks)
+  static constexpr int NIW_W = (BM / RPI) / NW;    // weight instructions per wave
+  static constexpr int STAGE = (BM + SK_BN) * ROWB;
+  static constexpr int RB = BM / 32;               // row blocks
+  static constexpr int KSL = NW / RB;              // k slices of a stage
   static constexpr int KS2 = BK / 16 / KSL;        // 32x32x16 k-steps per wave per stage
+  static_assert(NI % NW == 0 && (BM / RPI) % NW == 0 && NW % RB == 0, "work split");
   static constexpr int LDS = NST * STAGE;
   static_assert(NIW * (NST - 2) < 64, "vmcnt range");
   // Physical chunk = logical chunk ^ swz(row).  128-byte slices put two rows
@@ -162,13 +178,13 @@ struct SkGeom {
   static __device__ __forceinline__ int swz(int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & 7); }
 };
 
-template <int DT, int EPI, bool SPLIT, int BK, int NST>
+template <int DT, int EPI, bool SPLIT, int BK, int NST, int BM>
 __global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float* part, int kchunk,
                                                               int nsplit) {
   typedef typename Elt<DT>::T T;
-  typedef SkGeom<BK, NST, SK_NW> G;
+  typedef SkGeom<BK, NST, SK_NW, BM> G;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
-  constexpr int FB = SWI ? SK_BM / 2 : SK_BM;  // features per workgroup
+  constexpr int FB = SWI ? BM / 2 : BM;  // features per workgroup
   // One LDS object: the stage ring, reused at the end for the cross-wave sums.
   // (A second LDS variable gives the accesses alias scopes, and the wait-count
   // pass then waits for every outstanding DMA before each fragment read.)
@@ -186,7 +202,7 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float*
   const int nkt = (klen + BK - 1) / BK;
 
   // DMA: instruction i of a stage fills stage rows RPI*i .. RPI*i + RPI-1
-  // (rows 0..63 weights, 64..95 token slots); wave w issues i = w + NW j.  Lane
+  // (rows 0..BM-1 weights, then the 32 token slots); wave w issues i = w + NW j.  Lane
   // l: row RPI*i + l/CPR, physical chunk l%CPR, logical chunk phys ^ (row&15).
   // A chunk past the end of the K range (last stage of a range that is not a
   // multiple of BK) re-reads the range's first chunk instead; the k-steps that
@@ -200,16 +216,16 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float*
     const int r = G::RPI * i + lane / G::CPR;
     const int c = (lane % G::CPR) ^ G::swz(r);
     const T* row;
-    if (r < SK_BM) {
+    if (r < BM) {
       if constexpr (SWI) {
-        const int f = f0 + (r & 31);
-        row = reinterpret_cast<const T*>(r < 32 ? a.w[0] : a.w[1]) + (size_t)(f < a.N ? f : 0) * K;
+        const int f = f0 + (r < FB ? r : r - FB);
+        row = reinterpret_cast<const T*>(r < FB ? a.w[0] : a.w[1]) + (size_t)(f < a.N ? f : 0) * K;
       } else {
         const int f = f0 + r;
         row = seg_row<T>(a, f < a.N ? f : 0);
       }
     } else {
-      const int m = r - SK_BM;
+      const int m = r - BM;
       row = reinterpret_cast<const T*>(a.x) + (size_t)(m < a.M ? m : 0) * K;
     }
     src[j] = row + k0;
@@ -242,13 +258,13 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float*
     });
   };
 
-  // Fragments: wave w multiplies row block rb = w & 1 over the k-steps
-  // kh*KS2 .. kh*KS2 + KS2-1 (k slice kh = w >> 1) of every stage.
-  const int rb = wave & 1, kh = wave >> 1;
+  // Fragments: wave w multiplies row block rb = w % RB over the k-steps
+  // kh*KS2 .. kh*KS2 + KS2-1 (k slice kh = w / RB) of every stage.
+  const int rb = wave % G::RB, kh = wave / G::RB;
   const int l32 = lane & 31, h2 = lane >> 5;
   const int swz = G::swz(l32);  // rows rb*32 + l32 and token row 64 + l32 share it
   const int aoff = (rb * 32 + l32) * G::ROWB;
-  const int boff = SK_BM * G::ROWB + l32 * G::ROWB;
+  const int boff = BM * G::ROWB + l32 * G::ROWB;
 
   f32x16 acc;
 #pragma unroll
@@ -289,21 +305,22 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float*
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // k slices meet: waves 2.. hand their sums to waves 0, 1 (once every wave
-  // is done with the last stage, whose buffer may be the one reused).
+  // k slices meet: the waves of slices 1.. hand their sums to those of slice 0
+  // (once every wave is done with the last stage, whose buffer may be the one
+  // reused).
   __syncthreads();
-  if (kh > 0) red[((kh - 1) * 2 + rb) * 64 + lane] = acc;
+  if (kh > 0) red[((kh - 1) * G::RB + rb) * 64 + lane] = acc;
   __syncthreads();
   if (kh == 0) {
 #pragma unroll
-    for (int q = 0; q < G::KSL - 1; ++q) acc += red[(q * 2 + rb) * 64 + lane];
+    for (int q = 0; q < G::KSL - 1; ++q) acc += red[(q * G::RB + rb) * 64 + lane];
   }
   if constexpr (!SPLIT && SWI) {
-    // Gate rows are in wave 0, the matching up rows in wave 1.
+    // Gate rows are in row blocks 0 .. RB/2 - 1, the matching up rows RB/2 later.
     __syncthreads();
-    if (wave == 1) red[lane] = acc;
+    if (kh == 0 && rb >= G::RB / 2) red[(rb - G::RB / 2) * 64 + lane] = acc;
     __syncthreads();
-    if (wave != 0) return;
+    if (rb >= G::RB / 2) return;
   }
   if (kh > 0) return;
 
@@ -316,8 +333,8 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float*
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r = rb * 32 + g * 8 + h2 * 4;
-        const int f = SWI ? (r < 32 ? f0 + r : a.N + f0 + r - 32) : f0 + r;
-        if ((SWI ? f0 + (r & 31) : f) < a.N) {
+        const int f = SWI ? (r < FB ? f0 + r : a.N + f0 + r - FB) : f0 + r;
+        if ((SWI ? f0 + (r < FB ? r : r - FB) : f) < a.N) {
           f32x4 v = {acc[g * 4], acc[g * 4 + 1], acc[g * 4 + 2], acc[g * 4 + 3]};
           *reinterpret_cast<f32x4*>(p + f) = v;
         }
@@ -325,11 +342,11 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_dma_kernel(ProjArgs a, float*
     }
   } else if constexpr (SWI) {
     if (m >= a.M) return;
-    const f32x16 up = red[lane];
+    const f32x16 up = red[rb * 64 + lane];
     const float r = ssq.rstd(a);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int f = f0 + g * 8 + h2 * 4;
+      const int f = f0 + rb * 32 + g * 8 + h2 * 4;
       if (f >= a.N) continue;
       float v[4], u[4];
 #pragma unroll
@@ -666,35 +683,38 @@ bool gemv_dma_supported(int dt, int M, int K, int N) {
 int gemv_dma_norm_parts(int dt, bool w8, int M, int N_o, int K_o, int I) {
   if (dt != DT_BF16 || M <= 4 || N_o % 1024 != 0 || N_o / 1024 > SK_SSQ_MAX) return 0;
   if (!gemv_dma_supported(dt, M, K_o, N_o) || !gemv_dma_supported(dt, M, N_o, I)) return 0;
+  if (!w8 && sk_wide(EPI_RESID, N_o, K_o)) return 0;  // no split, no reduction
   int kchunk;
   const int ns = w8 ? sk_split_f(w8_features(EPI_RESID), N_o, K_o, &kchunk, W8_TARGET_WG)
                     : sk_split(EPI_RESID, N_o, K_o, &kchunk);
   return ns > 1 ? N_o / 1024 : 0;
 }
 
-template <int DT, int EPI, int BK, int NST>
-static hipError_t gemv_dma_cfg(const ProjArgs& a, hipStream_t s) {
+template <int DT, int EPI>
+static hipError_t gemv_dma_epi(const ProjArgs& a, hipStream_t s) {
+  if (sk_wide(EPI, a.N, a.K)) {
+    const int nblk = (a.N + sk_features(EPI, SK_BM_W) - 1) / sk_features(EPI, SK_BM_W);
+    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false, SK_BK_W, SK_NST_W, SK_BM_W>), dim3(nblk),
+              dim3(SK_NW * 64), 0, s, a, (float*)nullptr, a.K, 1);
+    return hipGetLastError();
+  }
   int kchunk;
   const int ns = sk_split(EPI, a.N, a.K, &kchunk);
   const int nblk = (a.N + sk_features(EPI) - 1) / sk_features(EPI);
   if (ns == 1) {
-    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false, BK, NST>), dim3(nblk), dim3(SK_NW * 64), 0, s, a,
-              (float*)nullptr, kchunk, 1);
+    LL_LAUNCH((gemv_dma_kernel<DT, EPI, false, SK_BK, SK_NST, SK_BM>), dim3(nblk), dim3(SK_NW * 64),
+              0, s, a, (float*)nullptr, kchunk, 1);
     return hipGetLastError();
   }
   if (!a.part) return hipErrorInvalidValue;
-  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true, BK, NST>), dim3(nblk * ns), dim3(SK_NW * 64), 0, s, a, a.part,
-            kchunk, ns);
+  LL_LAUNCH((gemv_dma_kernel<DT, EPI, true, SK_BK, SK_NST, SK_BM>), dim3(nblk * ns), dim3(SK_NW * 64),
+            0, s, a, a.part, kchunk, ns);
   const int n = ((a.N + 3) / 4) * a.M;
   LL_LAUNCH((gemv_split_reduce_kernel<DT, EPI>), dim3((n + 255) / 256), dim3(256), 0, s, a,
             (const float*)a.part, ns);
   return hipGetLastError();
 }
 
-template <int DT, int EPI>
-static hipError_t gemv_dma_epi(const ProjArgs& a, hipStream_t s) {
-  return gemv_dma_cfg<DT, EPI, SK_BK, SK_NST>(a, s);
-}
 
 template <int DT, int EPI>
 static hipError_t gemv_dma_w8_epi(const ProjArgs& a, hipStream_t s) {
