@@ -9,11 +9,13 @@
 // 64 KB of weights.  The eight waves split a stage's work as 2 row blocks x 4
 // k slices of v_mfma_f32_32x32x16; the k slices meet in LDS at the end (four
 // waves with k halves: 70B gate/up at 32 tokens 155.5 -> 154.0 us, step
-// 380.5 -> 377.3 us).
-// Measured on the 70B gate/up at 32 tokens against 64-k stages four deep with
-// three workgroups per CU (128-byte slices, 384 bytes per row in flight):
-// 183 -> 173 us; 128-k stages six deep (one workgroup per CU) were slower
-// (196 us), three deep with two workgroups per CU in between (176 us).
+// 380.5 -> 377.3 us).  Launches without a K split take a 128-row shape with
+// 128-k stages four deep instead (see the shape constants below).
+// Measured on the 70B gate/up at 32 tokens (four waves, 64 rows) against
+// 64-k stages four deep with three workgroups per CU (128-byte slices, 384
+// bytes per row in flight): 183 -> 173 us; 128-k stages six deep (one
+// workgroup per CU) were slower (196 us), three deep with two workgroups per
+// CU in between (176 us).
 //
 // The 16-byte chunks of a row slice are stored XOR-swizzled by (row & 15),
 // which makes the fragment reads conflict-free: the 16 rows one ds_read_b128
