@@ -179,6 +179,20 @@ def test_decode_deferred_ffn_norm(label, act, x_scale, norm_passes):
     assert launches == norm_passes, (label, launches)
 
 
+@pytest.mark.parametrize("label,shape", [
+    # K = 1088: the last 128-k stage is half empty (no stage rotation)
+    ("wide-gate-up-partial-stage", S.Shape(1088, 17, 1, 64, 16424)),
+    # K = 1024: eight whole stages, rotated by workgroup
+    ("wide-gate-up-rotated", S.Shape(1024, 8, 2, 128, 16424)),
+])
+def test_decode_32_tokens_wide_gate_up(label, shape):
+    """32 tokens with an intermediate size of 16424: gate/up has 257 blocks of
+    64 features, so it runs unsplit in the 128-row streaming shape, its last
+    workgroup holding 40 features."""
+    ctx = list(np.random.Generator(np.random.PCG64(11)).integers(0, 200, 32))
+    run_decode_case(label, shape, "bf16", "f16", ctx, 256, 170)
+
+
 def test_f16_decode_mha():
     run_decode_case("f16-decode", S.Shape(256, 4, 4, 64, 768), "f16", "f16", [10, 129], 160, 112)
 
