@@ -33,9 +33,8 @@ namespace ll {
 // Two workgroup shapes: 64 weight rows in 256-k stages three deep (144 KB of
 // LDS), and 128 rows in 128-k stages four deep (160 KB, 96 KB of weights in
 // flight per CU).  The 128-row shape serves launches that need no K split
-// (70B gate/up at 32 tokens: 153.5 -> 141.1 us, step 374.6 -> 363.7 us);
-// K-split launches keep 64 rows (O, down and QKV were each ~1 us slower with
-// 128).
+// (70B gate/up at 32 tokens: 153.0 -> 141.8 us); K-split launches keep 64
+// rows (O, down and QKV were each ~1 us slower with 128).
 constexpr int SK_BM = 64;                          // weight rows per workgroup
 constexpr int SK_BK = 256;                         // k per stage
 constexpr int SK_NST = 3;                          // stages in LDS
